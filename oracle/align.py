@@ -1,0 +1,72 @@
+"""Reference token-to-expert sort and padding for the indexed MoE path.  TEST INFRASTRUCTURE ONLY.
+
+"Humming" (wiki article), "Device and workload selection": the indexed path gathers
+input rows through routing indices.  The pages give no more than that, so every rule
+below is a reading (each is listed in the design notes).  Stability makes the
+result unique, so the GPU output must equal it byte for byte.
+
+Inputs: ``topk_ids`` int32 [T, topk]; flat index f = t*topk + j.  E experts, block size BM.
+
+1. cnt[e] = number of f with ids[f] == e (ids outside [0, E) are dropped).
+2. pad[e] = ceil(cnt[e] / BM) * BM (empty experts get no block).
+3. off[e] = exclusive prefix sum of pad in ascending e.
+4. sorted_ids[off[e] + i] = the i-th smallest f routed to e (stable, ascending f);
+   sorted_ids[off[e] + cnt[e] .. off[e] + pad[e] - 1] = sentinel T*topk.
+5. expert_ids[b] = e for every block b in [off[e]/BM, (off[e] + pad[e])/BM).
+6. num_post_pad = sum(pad).
+7. Up to capacity: sorted_ids = sentinel, expert_ids = -1.
+
+Capacity (worst case over all routings with the given T, topk, E, BM):
+cap_sorted = roundup(T*topk + min(E, T*topk) * (BM - 1), BM), cap_blocks = cap_sorted / BM.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def capacity(t: int, topk: int, experts: int, block_m: int):
+    tk = t * topk
+    raw = tk + min(experts, tk) * (block_m - 1)
+    cap_sorted = (raw + block_m - 1) // block_m * block_m
+    return cap_sorted, cap_sorted // block_m
+
+
+def moe_align(topk_ids, experts: int, block_m: int):
+    """Vectorised reference (counting sort).  Returns (sorted_ids, expert_ids, num_post_pad)."""
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    tk = ids.size
+    t, topk = np.asarray(topk_ids).shape
+    cap_sorted, cap_blocks = capacity(t, topk, experts, block_m)
+    valid = (ids >= 0) & (ids < experts)
+    cnt = np.bincount(ids[valid], minlength=experts)[:experts]
+    pad = (cnt + block_m - 1) // block_m * block_m
+    off = np.concatenate([[0], np.cumsum(pad)[:-1]])
+    sorted_ids = np.full(cap_sorted, tk, dtype=np.int32)
+    expert_ids = np.full(cap_blocks, -1, dtype=np.int32)
+    for e in range(experts):
+        f = np.nonzero(ids == e)[0]          # ascending f: the stable order
+        sorted_ids[off[e]:off[e] + f.size] = f
+        expert_ids[off[e] // block_m:(off[e] + pad[e]) // block_m] = e
+    return sorted_ids, expert_ids, int(pad.sum())
+
+
+def moe_align_bruteforce(topk_ids, experts: int, block_m: int):
+    """Pure-Python loops, for pinning the vectorised version on tiny inputs."""
+    t, topk = np.asarray(topk_ids).shape
+    flat = [int(v) for v in np.asarray(topk_ids).reshape(-1)]
+    tk = len(flat)
+    cap_sorted, cap_blocks = capacity(t, topk, experts, block_m)
+    sorted_ids = [tk] * cap_sorted
+    expert_ids = [-1] * cap_blocks
+    pos = 0
+    for e in range(experts):
+        mine = [f for f in range(tk) if flat[f] == e]
+        if not mine:
+            continue
+        nblk = -(-len(mine) // block_m)
+        for i, f in enumerate(mine):
+            sorted_ids[pos + i] = f
+        for b in range(nblk):
+            expert_ids[pos // block_m + b] = e
+        pos += nblk * block_m
+    return np.array(sorted_ids, np.int32), np.array(expert_ids, np.int32), pos

@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the quantized GEMM workloads.
+
+This module only *draws* inputs: random codes, scales, zero points, activations and
+routing choices, in the storage formats the library consumes (raw bit patterns in
+integer arrays).  It contains none of the GEMM arithmetic: no dequantization, no
+products, no sums.  Both the product path (tests and the benchmark upload these
+arrays to the GPU) and the CPU oracle (which decodes the same bits itself) consume
+what it returns.
+
+Storage formats produced (all row-major numpy arrays):
+
+* int4 / uint4 weights: ``uint32 [E, N, K/8]``; element (n, k) sits in bits
+  ``4*(k % 8) .. 4*(k % 8)+3`` of word ``[n, k // 8]`` (low nibble first).  Signed
+  int4 is stored as the two's-complement nibble.
+* e2m1 weights: ``uint8 [E, N, K/2]``; even k in the low nibble.
+* e4m3 (OCP "fn" flavour) weights / activations: ``uint8`` codes.
+* f16 / bf16 values: ``uint16`` bit patterns.
+* UE8M0 scales: ``uint8`` biased exponents.
+* zero points: ``uint8 [E, N, K/G]`` holding 0..15.
+* routing: ``int32 [T, topk]`` expert ids.
+
+The value distributions and shapes follow the five benchmark workloads: dense
+W4A16 (symmetric fp16 and asymmetric bf16), dense W8A8 FP8, MoE W4A16 with MXFP4
+weights and MoE W4A8 with int4 weights under a skewed router.  Draw order inside
+one workload is fixed: activations, codes, scales, zeros, routing logits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bfloat16 (torch's cast), returned as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> float16, returned as uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> OCP e4m3 codes (torch's cast). Input must already be clamped."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def absmax_e4m3_rows(x: np.ndarray):
+    """Per-row absmax quantization to e4m3 (input generation for the FP8 workloads).
+
+    scale = max|row| / 448 in float32 (1.0 for an all-zero row); code = RNE_e4m3(clamp(x / scale)).
+    Returns (codes uint8 [R, C], scale float32 [R]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    q = (x / scale[:, None]).astype(np.float32)
+    q = np.clip(q, -E4M3_MAX, E4M3_MAX)
+    return f32_to_e4m3_codes(q), scale
+
+
+def pack_nibbles_u32(nib: np.ndarray) -> np.ndarray:
+    """[.., K] values 0..15 -> uint32 [.., K/8], element k at bits 4*(k%8) (low nibble first)."""
+    nib = np.asarray(nib, dtype=np.uint32)
+    *lead, k = nib.shape
+    assert k % 8 == 0
+    v = nib.reshape(*lead, k // 8, 8)
+    out = np.zeros((*lead, k // 8), dtype=np.uint32)
+    for i in range(8):
+        out |= v[..., i] << np.uint32(4 * i)
+    return out
+
+
+def pack_nibbles_u8(nib: np.ndarray) -> np.ndarray:
+    """[.., K] values 0..15 -> uint8 [.., K/2], even k in the low nibble."""
+    nib = np.asarray(nib, dtype=np.uint8)
+    *lead, k = nib.shape
+    assert k % 2 == 0
+    v = nib.reshape(*lead, k // 2, 2)
+    return (v[..., 0] | (v[..., 1] << 4)).astype(np.uint8)
+
+
+def topk_from_logits(logits: np.ndarray, topk: int) -> np.ndarray:
+    """Top-k expert ids by descending logit (softmax is monotone, so this is softmax top-k).
+
+    Ties go to the lower expert id (stable sort).  Slot order is descending logit.
+    """
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return order[:, :topk].astype(np.int32)
+
+
+@dataclass
+class Layer:
+    """One quantized layer in storage form plus its activations."""
+    name: str
+    w_type: str            # "int4" | "uint4" | "e2m1" | "e4m3"
+    a_type: str            # "f16" | "bf16" | "e4m3"
+    s_type: str            # "f16" | "bf16" | "f32" | "ue8m0"
+    out_type: str          # "f16" | "bf16"
+    n: int
+    k: int
+    group: int             # 0 = per output channel
+    experts: int
+    w: np.ndarray          # packed codes, see module doc
+    s: np.ndarray          # scales: uint16 bits / float32 / uint8 exponents, [E, N, G]
+    z: np.ndarray | None   # uint8 [E, N, G] or None
+    compute: str = "native"  # "native" | "w_to_fp8"
+    meta: dict = field(default_factory=dict)
+
+
+@dataclass
+class Acts:
+    x: np.ndarray                  # uint16 bits [M, K] (f16/bf16) or uint8 e4m3 codes [M, K]
+    x_scale: np.ndarray | None     # float32 [M] for e4m3 activations
+    topk_ids: np.ndarray | None    # int32 [T, topk] for MoE
+
+
+# ---------------------------------------------------------------------------
+# Workloads.  Names describe what they are; sizes are arguments.
+# ---------------------------------------------------------------------------
+
+def dense_w4a16_sym_f16(m: int = 16, n: int = 512, k: int = 1024, group: int = 128, seed: int = 0):
+    """Dense W4A16, symmetric int4 in [-8, 7], fp16 group scales in [0.005, 0.02], fp16 activations."""
+    rng = _rng(seed)
+    x = f32_to_f16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    q = rng.integers(-8, 8, size=(1, n, k), dtype=np.int64)
+    s = f32_to_f16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
+    w = pack_nibbles_u32((q & 0xF).astype(np.uint32))
+    layer = Layer("dense_w4a16_sym_f16", "int4", "f16", "f16", "f16", n, k, group, 1, w, s, None)
+    return layer, Acts(x, None, None)
+
+
+def dense_w4a16_asym_bf16(m: int = 16, n: int = 8192, k: int = 8192, group: int = 128, seed: int = 0):
+    """Dense W4A16, uint4 codes in [0, 15] with uint4 zero points in [6, 9], bf16 group scales."""
+    rng = _rng(seed)
+    x = f32_to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    u = rng.integers(0, 16, size=(1, n, k), dtype=np.int64)
+    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
+    z = rng.integers(6, 10, size=(1, n, k // group), dtype=np.int64).astype(np.uint8)
+    w = pack_nibbles_u32(u.astype(np.uint32))
+    layer = Layer("dense_w4a16_asym_bf16", "uint4", "bf16", "bf16", "bf16", n, k, group, 1, w, s, z)
+    return layer, Acts(x, None, None)
+
+
+def dense_w8a8_fp8(m: int = 1, n: int = 7168, k: int = 7168, seed: int = 0):
+    """Dense W8A8: per-token absmax e4m3 activations, per-channel absmax e4m3 weights (N(0, 0.02))."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_rows(rng.standard_normal((m, k), dtype=np.float32))
+    wf = (rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    wq, sw = absmax_e4m3_rows(wf)
+    layer = Layer("dense_w8a8_fp8", "e4m3", "e4m3", "f32", "bf16", n, k, 0, 1,
+                  wq.reshape(1, n, k), sw.reshape(1, n, 1), None)
+    return layer, Acts(xq, sx, None)
+
+
+def moe_w4a16_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096, k: int = 7168,
+                    seed: int = 0):
+    """MoE W4A16 with MXFP4 weights: e2m1 codes uniform over all 16 codes, UE8M0 exponents 119..123
+    per 32 elements along K, bf16 activations, softmax top-k routing of N(0,1) logits."""
+    rng = _rng(seed)
+    x = f32_to_bf16_bits(rng.standard_normal((t, k), dtype=np.float32))
+    w = rng.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(experts, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    layer = Layer("moe_w4a16_mxfp4", "e2m1", "bf16", "ue8m0", "bf16", n, k, 32, experts, w, s, None)
+    return layer, Acts(x, None, ids)
+
+
+def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, k: int = 4096,
+                  group: int = 128, hot_frac: float = 0.2, hot_experts=(0, 1, 2, 3), hot_bias: float = 3.0,
+                  seed: int = 0):
+    """MoE W4A8: symmetric int4 weights in [-8, 7] with bf16 group-128 scales (converted to e4m3 inside
+    the kernel), per-token absmax e4m3 activations, and a skewed router: a seeded 20% of tokens get
+    +3.0 on the logits of four hot experts before top-k."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_rows(rng.standard_normal((t, k), dtype=np.float32))
+    q = rng.integers(-8, 8, size=(experts, n, k), dtype=np.int64)
+    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(experts, n, k // group)).astype(np.float32))
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    n_hot = int(round(hot_frac * t))
+    hot_tokens = rng.permutation(t)[:n_hot]
+    for e in hot_experts:
+        if e < experts:
+            logits[hot_tokens, e] += np.float32(hot_bias)
+    ids = topk_from_logits(logits, topk)
+    w = pack_nibbles_u32((q & 0xF).astype(np.uint32))
+    layer = Layer("moe_w4a8_int4", "int4", "e4m3", "bf16", "bf16", n, k, group, experts, w, s, None,
+                  compute="w_to_fp8")
+    return layer, Acts(xq, sx, ids)
+
+
+WORKLOADS = {
+    "dense_w4a16_sym_f16": dense_w4a16_sym_f16,
+    "dense_w4a16_asym_bf16": dense_w4a16_asym_bf16,
+    "dense_w8a8_fp8": dense_w8a8_fp8,
+    "moe_w4a16_mxfp4": moe_w4a16_mxfp4,
+    "moe_w4a8_int4": moe_w4a8_int4,
+}
