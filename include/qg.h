@@ -1,0 +1,209 @@
+/*
+ * qg.h -- C ABI of the MI355X (gfx950) quantized GEMM library (libqg.so).
+ *
+ * What it computes: Y = X . dequant(Wq, scales, zeros)^T with low-bit weights
+ * (int4 / uint4 + zero points, FP4 e2m1 with UE8M0 block scales, FP8 e4m3 with
+ * channel scales) and f16 / bf16 / FP8 e4m3 activations, as a dense layer and as
+ * an MoE grouped GEMM over routed tokens.  Sources: the web pages on the Humming
+ * quantized-GEMM library -- "Humming" (README), "Key Features" and "Support Matrix"
+ * (weight, activation and scale types; dense and MoE GEMM); "Humming: Fast,
+ * Flexible Kernels for Quantized Inference" (the standard format of weights,
+ * scales and zero points; preprocessing that repacks tensors into the kernel's
+ * layout); "Humming" (wiki article), "Quantization representation", "Kernel
+ * configuration and compilation" and "Device and workload selection" (channel /
+ * group / block scales, arch-tied transformed layouts, M-range dispatch, the
+ * indexed MoE path).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers unless stated otherwise; descriptors and
+ *   handles are HOST structs.  The caller owns every allocation; the library never
+ *   allocates or frees device memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call only enqueues work on that stream and returns; there is no host
+ *   synchronisation on any path (MoE grids are sized from capacity, not counts).
+ * - Arguments are validated on the host BEFORE anything is launched.  On error
+ *   nothing is written and the status says why; the library never prints (unless
+ *   the environment variable QG_LOG=1) and never throws across the ABI.
+ * - QG_ERR_HIP is returned when a launch reports an error (hipGetLastError).
+ * - M == 0 (or T == 0) is a successful no-op.
+ * - Row-major tensors with contiguous rows; every pointer must be 16-byte aligned.
+ * - Shape rules: n % 64 == 0, k % 256 == 0, k % group_k == 0.
+ */
+#ifndef QG_H_
+#define QG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QG_OK = 0,
+  QG_ERR_INVALID_ARG = 1,    /* null / misaligned pointer, negative size, bad enum value      */
+  QG_ERR_UNSUPPORTED = 2,    /* valid but unsupported type combination or shape               */
+  QG_ERR_ARCH_MISMATCH = 3,  /* prepared for another GPU architecture than the current device */
+  QG_ERR_NOT_PREPARED = 4,   /* handle not filled by qg_prepare (magic / layout version)      */
+  QG_ERR_WORKSPACE = 5,      /* workspace or output buffer too small                           */
+  QG_ERR_CAPACITY = 6,       /* MoE align buffers smaller than the worst-case capacity         */
+  QG_ERR_HIP = 7             /* a HIP call or kernel launch failed                             */
+} qg_status;
+
+/* Weight storage types (logical layouts are those accepted by qg_prepare). */
+enum { QG_W_INT4 = 1,      /* symmetric int4 in [-8, 7], two's-complement nibbles            */
+       QG_W_UINT4 = 2,     /* uint4 in [0, 15]; with has_zero, value (u - z) * s              */
+       QG_W_FP4_E2M1 = 3,  /* OCP FP4 e2m1 codes                                              */
+       QG_W_FP8_E4M3 = 4   /* OCP FP8 e4m3 ("fn") codes                                       */ };
+/* Scale types. */
+enum { QG_S_F16 = 1, QG_S_BF16 = 2, QG_S_F32 = 3, QG_S_UE8M0 = 4 };
+/* Activation types.  FP8 activations come with one float32 scale per row (token). */
+enum { QG_A_F16 = 1, QG_A_BF16 = 2, QG_A_FP8_E4M3 = 3 };
+/* Output types. */
+enum { QG_O_F16 = 1, QG_O_BF16 = 2 };
+/* Compute options. */
+enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                               */
+       QG_C_W_TO_FP8 = 1   /* int4 weights converted to e4m3 in-kernel (FP8 activations)      */ };
+
+/*
+ * Layer description ("Layer config": shapes, data types, quantization parameters).
+ * Supported combinations (anything else -> QG_ERR_UNSUPPORTED):
+ *   int4 / uint4(+zeros) weights, f16|bf16 scales, group_k a multiple of 128 or 0
+ *       (per channel), f16|bf16 activations                          [W4A16]
+ *   int4 weights, QG_C_W_TO_FP8, bf16|f16 group-128-multiple scales, e4m3 acts [W4A8]
+ *   e2m1 weights, UE8M0 scales, group_k == 32, f16|bf16 activations  [MXFP4 W4A16]
+ *   e4m3 weights, f32 channel scales (group_k == 0), e4m3 activations [W8A8]
+ */
+typedef struct {
+  int32_t w_type;       /* QG_W_*                                                      */
+  int32_t s_type;       /* QG_S_*                                                      */
+  int32_t group_k;      /* elements per scale along K; 0 = one scale per output channel */
+  int32_t has_zero;     /* 1: uint4 zero point per (n, group), only with QG_W_UINT4    */
+  int32_t a_type;       /* QG_A_*                                                      */
+  int32_t compute;      /* QG_C_*                                                      */
+  int32_t out_type;     /* QG_O_*                                                      */
+  int32_t num_experts;  /* 1 for a dense layer                                         */
+  int64_t n;            /* output features                                             */
+  int64_t k;            /* reduction dimension                                         */
+} qg_layer_desc;
+
+/*
+ * Prepared-layer handle: a caller-owned host POD filled by qg_prepare.  It records
+ * the target architecture (the prepared layout is tied to it) and where the
+ * weight, scale and zero regions live inside the caller's device buffer.
+ */
+typedef struct {
+  uint32_t magic;            /* 'QGP1' once prepared                                */
+  uint32_t layout_version;   /* 1                                                   */
+  uint32_t gfx_arch;         /* 950 for gfx950                                      */
+  uint32_t reserved;
+  qg_layer_desc desc;
+  void* dev;                 /* device buffer holding the prepared image            */
+  uint64_t bytes;            /* size of that image                                  */
+  uint64_t off_w, off_s, off_z;                 /* region offsets in bytes           */
+  uint64_t w_expert_bytes, s_expert_bytes, z_expert_bytes;  /* per-expert strides    */
+} qg_prepared;
+
+#define QG_PREPARED_MAGIC 0x31504751u   /* "QGP1" little-endian */
+#define QG_LAYOUT_VERSION 1u
+
+/*
+ * qg_prepared_bytes: device bytes qg_prepare needs for `desc`; 0 if the
+ * description is invalid or unsupported.  Host-only, never touches the GPU.
+ */
+size_t qg_prepared_bytes(const qg_layer_desc* desc);
+
+/*
+ * qg_prepare: the offline transform ("transform()" in the pages: validate, then
+ * repack weights, scales and zeros into the layout the kernels read).  One
+ * prepared image serves every M and every tile choice.
+ *   w      device, logical weights of all experts, contiguous:
+ *            int4/uint4  uint32 [E][N][K/8]  (element k at bits 4*(k%8), low nibble first)
+ *            e2m1        uint8  [E][N][K/2]  (even k in the low nibble)
+ *            e4m3        uint8  [E][N][K]
+ *   scales device, [E][N][G] of the scale type (G = K/group_k, or 1 per channel)
+ *   zeros  device, uint8 [E][N][G] holding 0..15 when has_zero, else NULL
+ *   dev_out device buffer of at least qg_prepared_bytes(desc) bytes (must not
+ *          overlap the inputs); `out` (host) receives the handle.
+ * Enqueued on `stream`; the inputs may be freed once the stream has passed it.
+ */
+qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scales, const void* zeros,
+                     void* dev_out, size_t dev_bytes, qg_prepared* out, void* stream);
+
+/*
+ * qg_workspace_bytes: device workspace qg_gemm / qg_moe_gemm need for m rows
+ * (dense) or T tokens x topk (MoE; pass topk = 0 for dense).  0 means none.
+ */
+size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk);
+
+/*
+ * qg_gemm: dense Y[m, n] = sum_k X[m, k] * W[n, k] for a prepared dense layer.
+ *   x        device [M][K] of a_type (f16/bf16 values or e4m3 codes)
+ *   x_scale  device float32 [M] per-token scales for e4m3 activations, else NULL
+ *   y        device [M][N] of out_type, written in full (fp32 accumulation, RNE)
+ *   ws       device workspace of ws_bytes >= qg_workspace_bytes(p, m, 0)
+ * The tile / split-K choice is made from M on the host (the M-bucket selector).
+ */
+qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, void* y, int64_t m,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MoE routing preparation (the indexed input path: rows are gathered through
+ * routing indices).  qg_moe_block_m returns the row-block size the grouped GEMM
+ * will use for T tokens with topk slots (0 on an invalid handle).
+ * qg_moe_capacity returns the worst-case buffer sizes for any routing:
+ *   cap_sorted = roundup(T*topk + min(E, T*topk)*(block_m - 1), block_m),
+ *   cap_blocks = cap_sorted / block_m.
+ */
+int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk);
+qg_status qg_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t block_m,
+                          int64_t* cap_sorted, int64_t* cap_blocks);
+
+/*
+ * qg_moe_align: token-to-expert sort and padding.
+ *   topk_ids   device int32 [T][topk]; flat index f = t*topk + j; ids outside [0, E) are dropped
+ *   sorted_ids device int32 [cap_sorted]: for each expert e in ascending order, the flat
+ *              indices routed to e in ascending order, padded with the sentinel T*topk to a
+ *              multiple of block_m; sentinel after the end
+ *   expert_ids device int32 [cap_blocks]: expert of each block_m-row block, -1 after the end
+ *   num_post_pad device int32 [1]: total padded rows
+ * Deterministic: the result is unique and bit-exact.  Capacities below
+ * qg_moe_capacity -> QG_ERR_CAPACITY.  block_m must be a power of two in [1, 256].
+ */
+qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts,
+                       int32_t block_m, int32_t* sorted_ids, int64_t cap_sorted, int32_t* expert_ids,
+                       int64_t cap_blocks, int32_t* num_post_pad, void* stream);
+
+/*
+ * qg_moe_gemm: grouped GEMM over the aligned rows.  For every (token t, slot j)
+ * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
+ *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3, else NULL
+ *   sorted_ids / expert_ids / num_post_pad  from qg_moe_align with the same block_m
+ *   y        device [T*topk][N] of out_type; rows of dropped slots are not written
+ * The grid is sized from capacity; blocks past num_post_pad exit at once.
+ */
+qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
+                      const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
+                      int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qg_dequant: writes expert `expert` of a prepared layer back as dense float32
+ * [N][K] = code value (minus zero point) times scale, read through the same
+ * unpack routines the GEMM kernels use.  Every such value is exact in float32
+ * except e4m3 x f32 channel scale, which is one correctly rounded product.
+ * For checking the prepared layout; not on the GEMM path.
+ */
+qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* qg_status_str(qg_status s);
+
+/* Library / layout version: (major << 16) | minor. */
+int32_t qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QG_H_ */

@@ -1,0 +1,376 @@
+// Host side of libqg.so: the C ABI declared in include/qg.h.  Validation happens
+// here, before anything is launched; then the M-bucket selector picks a kernel
+// family and tile ("Humming" wiki article, "Device and workload selection": ranges of
+// M get their own configurations, chosen by where computation starts to dominate
+// weight transfer) and the launch is enqueued on the caller's stream.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "qg.h"
+#include "qg_device.h"
+#include "qg_kernels.h"
+
+using namespace qg;
+
+namespace {
+
+bool log_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("QG_LOG");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+#define QG_LOG(...)                         \
+  do {                                      \
+    if (log_enabled()) {                    \
+      fprintf(stderr, "[qg] " __VA_ARGS__); \
+      fputc('\n', stderr);                  \
+    }                                       \
+  } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Architecture of the current device: 950 for gfx950, 0 if unknown, -1 on error.
+int current_arch() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 64 && init[dev]) return cached[dev];
+  hipDeviceProp_t prop;
+  int arch = -1;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess) arch = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 950 : 0;
+  if (dev < 64) { cached[dev] = arch; init[dev] = true; }
+  return arch;
+}
+
+// Which kernel weight path a layer uses.
+struct PathInfo {
+  int wp_small;   // path of the weight-streaming kernel
+  int order;      // repack nibble order: 0 natural, 1 pair, 2 quad
+  int bias8;      // repack stores q + 8
+  int w4;         // 4-bit codes
+  int af, of, st;
+  int dq_wp;      // path used for the read-back check
+};
+
+int scale_bytes(int s_type) {
+  switch (s_type) {
+    case QG_S_F16: case QG_S_BF16: return 2;
+    case QG_S_F32: return 4;
+    case QG_S_UE8M0: return 1;
+    default: return 0;
+  }
+}
+
+// Host-only validation of a layer description.
+qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
+  if (!d) return QG_ERR_INVALID_ARG;
+  if (d->w_type < QG_W_INT4 || d->w_type > QG_W_FP8_E4M3) return QG_ERR_INVALID_ARG;
+  if (d->s_type < QG_S_F16 || d->s_type > QG_S_UE8M0) return QG_ERR_INVALID_ARG;
+  if (d->a_type < QG_A_F16 || d->a_type > QG_A_FP8_E4M3) return QG_ERR_INVALID_ARG;
+  if (d->out_type != QG_O_F16 && d->out_type != QG_O_BF16) return QG_ERR_INVALID_ARG;
+  if (d->compute != QG_C_NATIVE && d->compute != QG_C_W_TO_FP8) return QG_ERR_INVALID_ARG;
+  if (d->has_zero != 0 && d->has_zero != 1) return QG_ERR_INVALID_ARG;
+  if (d->n <= 0 || d->k <= 0 || d->num_experts <= 0 || d->group_k < 0) return QG_ERR_INVALID_ARG;
+  if (d->n % 64 != 0 || d->k % 256 != 0) return QG_ERR_UNSUPPORTED;
+  if (d->n > (1 << 30) || d->k > (1 << 20) || d->num_experts > 4096) return QG_ERR_UNSUPPORTED;
+  if (d->group_k != 0 && d->k % d->group_k != 0) return QG_ERR_UNSUPPORTED;
+  PathInfo p{};
+  p.of = d->out_type == QG_O_F16 ? O_F16 : O_BF16;
+  const bool act16 = d->a_type == QG_A_F16 || d->a_type == QG_A_BF16;
+  if (d->w_type == QG_W_INT4 || d->w_type == QG_W_UINT4) {
+    if (d->w_type == QG_W_UINT4 && !d->has_zero) return QG_ERR_UNSUPPORTED;
+    if (d->w_type == QG_W_INT4 && d->has_zero) return QG_ERR_UNSUPPORTED;
+    if (d->group_k != 0 && d->group_k % 128 != 0) return QG_ERR_UNSUPPORTED;
+    if (d->s_type != QG_S_F16 && d->s_type != QG_S_BF16) return QG_ERR_UNSUPPORTED;
+    p.w4 = 1;
+    if (act16 && d->compute == QG_C_NATIVE) {
+      // 16-bit activations: scale and output types follow the activation type
+      const int t = d->a_type == QG_A_F16 ? QG_S_F16 : QG_S_BF16;
+      if (d->s_type != t || d->out_type != (d->a_type == QG_A_F16 ? QG_O_F16 : QG_O_BF16)) return QG_ERR_UNSUPPORTED;
+      p.wp_small = WP_INT4_MAGIC; p.order = 1; p.bias8 = d->w_type == QG_W_INT4;
+      p.af = d->a_type == QG_A_F16 ? A_F16 : A_BF16;
+      p.dq_wp = WP_INT4_MAGIC;
+    } else if (d->a_type == QG_A_FP8_E4M3 && d->compute == QG_C_W_TO_FP8 && d->w_type == QG_W_INT4) {
+      if ((d->s_type == QG_S_BF16) != (d->out_type == QG_O_BF16)) return QG_ERR_UNSUPPORTED;
+      p.wp_small = WP_INT4Q_MAGIC; p.order = 2; p.bias8 = 0; p.af = A_FP8;
+      p.dq_wp = WP_INT4Q_FP8;
+    } else {
+      return QG_ERR_UNSUPPORTED;
+    }
+    p.st = d->s_type == QG_S_F16 ? S_F16 : S_BF16;
+  } else if (d->w_type == QG_W_FP4_E2M1) {
+    if (!act16 || d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 32 || d->s_type != QG_S_UE8M0)
+      return QG_ERR_UNSUPPORTED;
+    if (d->out_type != (d->a_type == QG_A_F16 ? QG_O_F16 : QG_O_BF16)) return QG_ERR_UNSUPPORTED;
+    p.wp_small = WP_FP4; p.order = 0; p.w4 = 1; p.af = d->a_type == QG_A_F16 ? A_F16 : A_BF16; p.st = S_UE8M0;
+    p.dq_wp = WP_FP4;
+  } else {  // e4m3
+    if (d->a_type != QG_A_FP8_E4M3 || d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 0 ||
+        d->s_type != QG_S_F32)
+      return QG_ERR_UNSUPPORTED;
+    p.wp_small = WP_FP8; p.w4 = 0; p.af = A_FP8; p.st = S_F32; p.dq_wp = WP_FP8;
+  }
+  if (pi) *pi = p;
+  return QG_OK;
+}
+
+struct Sizes { int64_t wb, sb, zb, off_s, off_z, total, groups; };
+
+Sizes sizes_of(const qg_layer_desc* d) {
+  Sizes s{};
+  const int bits = d->w_type == QG_W_FP8_E4M3 ? 8 : 4;
+  s.groups = d->group_k == 0 ? 1 : d->k / d->group_k;
+  s.wb = d->n * d->k * bits / 8;                     // per expert
+  s.sb = d->n * s.groups * scale_bytes(d->s_type);   // per expert
+  s.zb = d->has_zero ? (d->n / 16) * s.groups * 8 : 0;
+  const int64_t e = d->num_experts;
+  s.off_s = align256(e * s.wb);
+  s.off_z = s.off_s + align256(e * s.sb);
+  s.total = s.off_z + align256(e * s.zb);
+  return s;
+}
+
+qg_status check_prepared(const qg_prepared* p, PathInfo* pi) {
+  if (!p) return QG_ERR_INVALID_ARG;
+  if (p->magic != QG_PREPARED_MAGIC || p->layout_version != QG_LAYOUT_VERSION) return QG_ERR_NOT_PREPARED;
+  qg_status s = check_desc(&p->desc, pi);
+  if (s != QG_OK) return QG_ERR_NOT_PREPARED;
+  if (!p->dev || p->bytes < (uint64_t)sizes_of(&p->desc).total) return QG_ERR_NOT_PREPARED;
+  if (p->gfx_arch != 950) return QG_ERR_ARCH_MISMATCH;
+  return QG_OK;
+}
+
+qg_status check_arch() {
+  const int a = current_arch();
+  if (a < 0) return QG_ERR_HIP;
+  if (a != 950) return QG_ERR_ARCH_MISMATCH;
+  return QG_OK;
+}
+
+qg_status launched() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    QG_LOG("launch failed: %s", hipGetErrorString(e));
+    return QG_ERR_HIP;
+  }
+  return QG_OK;
+}
+
+// ---- M-bucket selector --------------------------------------------------------------
+// Weight-streaming family: one wave streams 2 column tiles (32 columns) of a chunk
+// range; KW waves share K inside a workgroup.
+StreamTile stream_tile(int64_t rows, int64_t n, int64_t k) {
+  StreamTile t{};
+  t.nt = 2;
+  t.ch = 8;
+  t.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const int64_t nchunks = k / 128;
+  t.kw = nchunks >= 8 ? 8 : (nchunks >= 4 ? 4 : 2);   // K beyond 8*8 chunks runs in rounds
+  t.grid_x = (unsigned)(n / (16 * t.nt));
+  t.grid_y = (unsigned)((rows + 16 * t.mt - 1) / (16 * t.mt));
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_str(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_INVALID_ARG: return "invalid argument";
+    case QG_ERR_UNSUPPORTED: return "unsupported type combination or shape";
+    case QG_ERR_ARCH_MISMATCH: return "prepared layout / device architecture mismatch";
+    case QG_ERR_NOT_PREPARED: return "handle not prepared by qg_prepare";
+    case QG_ERR_WORKSPACE: return "workspace or buffer too small";
+    case QG_ERR_CAPACITY: return "MoE align buffers below capacity";
+    case QG_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int32_t qg_version(void) { return (1 << 16) | 0; }
+
+size_t qg_prepared_bytes(const qg_layer_desc* desc) {
+  if (check_desc(desc, nullptr) != QG_OK) return 0;
+  return (size_t)sizes_of(desc).total;
+}
+
+qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scales, const void* zeros, void* dev_out,
+                     size_t dev_bytes, qg_prepared* out, void* stream) {
+  PathInfo pi;
+  qg_status s = check_desc(desc, &pi);
+  if (s != QG_OK) return s;
+  if (!w || !scales || !dev_out || !out) return QG_ERR_INVALID_ARG;
+  if (desc->has_zero && !zeros) return QG_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(dev_out) || ((uintptr_t)scales % scale_bytes(desc->s_type)) != 0)
+    return QG_ERR_INVALID_ARG;
+  const Sizes sz = sizes_of(desc);
+  if ((int64_t)dev_bytes < sz.total) return QG_ERR_WORKSPACE;
+  s = check_arch();
+  if (s != QG_OK) return s;
+  RepackArgs a{};
+  a.w = w; a.s = scales; a.z = (const uint8_t*)zeros;
+  a.out_w = (uint8_t*)dev_out;
+  a.out_s = (uint8_t*)dev_out + sz.off_s;
+  a.out_z = desc->has_zero ? (uint32_t*)((uint8_t*)dev_out + sz.off_z) : nullptr;
+  if (!desc->has_zero) a.z = nullptr;
+  a.experts = desc->num_experts; a.n = (int)desc->n; a.k = (int)desc->k; a.groups = (int)sz.groups;
+  a.w4 = pi.w4; a.order = pi.order; a.bias8 = pi.bias8; a.s_bytes = scale_bytes(desc->s_type);
+  launch_repack(a, (hipStream_t)stream);
+  s = launched();
+  if (s != QG_OK) return s;
+  qg_prepared p{};
+  p.magic = QG_PREPARED_MAGIC; p.layout_version = QG_LAYOUT_VERSION; p.gfx_arch = 950;
+  p.desc = *desc; p.dev = dev_out; p.bytes = (uint64_t)sz.total;
+  p.off_w = 0; p.off_s = (uint64_t)sz.off_s; p.off_z = (uint64_t)sz.off_z;
+  p.w_expert_bytes = (uint64_t)sz.wb; p.s_expert_bytes = (uint64_t)sz.sb; p.z_expert_bytes = (uint64_t)sz.zb;
+  *out = p;
+  QG_LOG("prepare n=%lld k=%lld experts=%d bytes=%lld", (long long)desc->n, (long long)desc->k,
+         desc->num_experts, (long long)sz.total);
+  return QG_OK;
+}
+
+size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk) {
+  (void)m_or_tokens; (void)topk;
+  if (check_prepared(p, nullptr) != QG_OK) return 0;
+  return 0;
+}
+
+static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
+  const uint8_t* base = (const uint8_t*)p->dev;
+  a.w = base + p->off_w;
+  a.s = base + p->off_s;
+  a.z = p->desc.has_zero ? (const uint32_t*)(base + p->off_z) : nullptr;
+  a.n = (int)p->desc.n; a.k = (int)p->desc.k; a.group = p->desc.group_k;
+  a.w_expert_bytes = (int64_t)p->w_expert_bytes;
+}
+
+qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, void* y, int64_t m, void* ws,
+                  size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  PathInfo pi;
+  qg_status s = check_prepared(p, &pi);
+  if (s != QG_OK) return s;
+  if (p->desc.num_experts != 1) return QG_ERR_UNSUPPORTED;
+  if (m < 0) return QG_ERR_INVALID_ARG;
+  if (m == 0) return QG_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return QG_ERR_INVALID_ARG;
+  if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
+  if (m > (1 << 24)) return QG_ERR_UNSUPPORTED;
+  s = check_arch();
+  if (s != QG_OK) return s;
+  StreamArgs a{};
+  fill_stream_args(a, p);
+  a.x = x; a.x_scale = x_scale; a.y = y; a.m = m;
+  const StreamTile t = stream_tile(m, p->desc.n, p->desc.k);
+  QG_LOG("gemm m=%lld n=%lld k=%lld -> stream mt=%d nt=%d kw=%d grid=%ux%u", (long long)m, (long long)p->desc.n,
+         (long long)p->desc.k, t.mt, t.nt, t.kw, t.grid_x, t.grid_y);
+  if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
+int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
+  if (check_prepared(p, nullptr) != QG_OK || tokens < 0 || topk <= 0) return 0;
+  const int64_t rows = tokens * topk;
+  const int64_t per_expert = (rows + p->desc.num_experts - 1) / p->desc.num_experts;
+  if (per_expert <= 16) return 16;
+  if (per_expert <= 32) return 32;
+  return 64;
+}
+
+qg_status qg_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t block_m, int64_t* cap_sorted,
+                          int64_t* cap_blocks) {
+  if (tokens < 0 || topk <= 0 || num_experts <= 0 || block_m <= 0 || !cap_sorted || !cap_blocks)
+    return QG_ERR_INVALID_ARG;
+  const int64_t tk = tokens * topk;
+  const int64_t raw = tk + (tk < num_experts ? tk : num_experts) * (int64_t)(block_m - 1);
+  *cap_sorted = (raw + block_m - 1) / block_m * block_m;
+  *cap_blocks = *cap_sorted / block_m;
+  return QG_OK;
+}
+
+qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts, int32_t block_m,
+                       int32_t* sorted_ids, int64_t cap_sorted, int32_t* expert_ids, int64_t cap_blocks,
+                       int32_t* num_post_pad, void* stream) {
+  if (tokens < 0 || topk <= 0 || num_experts <= 0) return QG_ERR_INVALID_ARG;
+  if (block_m <= 0 || block_m > 256 || (block_m & (block_m - 1)) != 0) return QG_ERR_INVALID_ARG;
+  if (num_experts > 512) return QG_ERR_UNSUPPORTED;
+  if (tokens * topk > (int64_t)1 << 30) return QG_ERR_UNSUPPORTED;
+  if (!sorted_ids || !expert_ids || !num_post_pad || (tokens > 0 && !topk_ids)) return QG_ERR_INVALID_ARG;
+  int64_t cs, cb;
+  qg_moe_capacity(tokens, topk, num_experts, block_m, &cs, &cb);
+  if (cap_sorted < cs || cap_blocks < cb) return QG_ERR_CAPACITY;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  launch_moe_align(topk_ids, (int)(tokens * topk), num_experts, block_m, sorted_ids, cap_sorted, expert_ids,
+                   cap_blocks, num_post_pad, (hipStream_t)stream);
+  return launched();
+}
+
+qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
+                      const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
+                      int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  PathInfo pi;
+  qg_status s = check_prepared(p, &pi);
+  if (s != QG_OK) return s;
+  if (tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARG;
+  if (tokens == 0) return QG_OK;
+  if (!x || !y || !sorted_ids || !expert_ids || !num_post_pad || !aligned16(x) || !aligned16(y))
+    return QG_ERR_INVALID_ARG;
+  if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
+  if (block_m != 16 && block_m != 32 && block_m != 64) return QG_ERR_UNSUPPORTED;
+  if (tokens * topk > (int64_t)1 << 30) return QG_ERR_UNSUPPORTED;
+  s = check_arch();
+  if (s != QG_OK) return s;
+  int64_t cs, cb;
+  qg_moe_capacity(tokens, topk, p->desc.num_experts, block_m, &cs, &cb);
+  StreamArgs a{};
+  fill_stream_args(a, p);
+  a.x = x; a.x_scale = x_scale; a.y = y; a.m = 0;
+  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.num_post_pad = num_post_pad;
+  a.topk = topk; a.sentinel = (int)(tokens * topk);
+  StreamTile t = stream_tile(block_m, p->desc.n, p->desc.k);
+  t.grid_y = (unsigned)cb;
+  QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> stream mt=%d kw=%d grid=%ux%u", (long long)tokens, topk, block_m, t.mt,
+         t.kw, t.grid_x, t.grid_y);
+  if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
+qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* stream) {
+  PathInfo pi;
+  qg_status s = check_prepared(p, &pi);
+  if (s != QG_OK) return s;
+  if (expert < 0 || expert >= p->desc.num_experts || !out) return QG_ERR_INVALID_ARG;
+  s = check_arch();
+  if (s != QG_OK) return s;
+  const uint8_t* base = (const uint8_t*)p->dev;
+  DequantArgs a{};
+  a.w = base + p->off_w + (int64_t)expert * p->w_expert_bytes;
+  a.s = base + p->off_s + (int64_t)expert * p->s_expert_bytes;
+  a.z = p->desc.has_zero ? (const uint32_t*)(base + p->off_z + (int64_t)expert * p->z_expert_bytes) : nullptr;
+  a.out = out;
+  a.n = (int)p->desc.n; a.k = (int)p->desc.k;
+  a.groups = p->desc.group_k == 0 ? 1 : (int)(p->desc.k / p->desc.group_k);
+  a.group = p->desc.group_k;
+  a.wp = pi.dq_wp; a.af = pi.af; a.stype = pi.st; a.zero = p->desc.has_zero;
+  launch_dequant(a, (hipStream_t)stream);
+  return launched();
+}
+
+}  // extern "C"

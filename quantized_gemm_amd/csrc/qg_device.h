@@ -1,0 +1,179 @@
+// Device-side building blocks for the gfx950 quantized GEMM kernels: vector types,
+// MFMA wrappers, bit-unpack / dequant routines for the prepared layout, loads.
+//
+// Prepared layout (format version 1; the transform is "preprocessing ... repacks
+// these tensors into layouts suited to the target kernel" in "Humming: Fast, Flexible
+// Kernels for Quantized Inference"):
+//   W: 16-byte units [e][n/16][k/KU][n%16], KU = 32 (4-bit) or 16 (e4m3).  A 4-bit unit is
+//      four u32 words; word j holds k = 8j..8j+7 of the unit, nibble position p holding
+//      element ORDER[p]:  PAIR {0,2,4,6,1,3,5,7} (int4/uint4 with f16/bf16 activations;
+//      int4 stored biased, q + 8), QUAD {0,4,1,5,2,6,3,7} (int4 for the e4m3 conversion,
+//      two's complement), NATURAL (e2m1).
+//   S: [e][n/16][group][n%16] scale elements.  Z: [e][n/16][group] two u32 words of
+//      16 nibbles (column c at word c/8, nibble c%8).
+// One 16-byte unit is exactly what one lane loads, so every kernel reads the weight
+// stream with 16-byte, fully coalesced loads whatever its tile shape.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Formats (template tags) ---------------------------------------------------------
+enum : int { A_F16 = 1, A_BF16 = 2, A_FP8 = 3 };
+enum : int { O_F16 = 1, O_BF16 = 2 };
+enum : int { S_F16 = 1, S_BF16 = 2, S_F32 = 3, S_UE8M0 = 4 };
+// Weight paths of the kernels.
+enum : int {
+  WP_INT4_MAGIC = 1,   // int4/uint4 (PAIR order) -> 16-bit operand 1 + u/2^p, zero/scale applied per group
+  WP_INT4Q_MAGIC = 2,  // int4 (QUAD order, two's complement) -> 16-bit operand, A permuted to match
+  WP_FP4 = 3,          // e2m1 -> bf16/f16 with the UE8M0 block scale folded in
+  WP_FP8 = 4,          // e4m3 used as is, fp8 MFMA
+  WP_INT4Q_FP8 = 5     // int4 (QUAD) -> e4m3 by table, fp8 MFMA, group scale per 128-k MFMA
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+template <int ST>
+__device__ __forceinline__ float scale_to_f32(const void* base, int64_t idx) {
+  if constexpr (ST == S_F16) return f16_bits_to_f32(((const uint16_t*)base)[idx]);
+  else if constexpr (ST == S_BF16) return bf16_bits_to_f32(((const uint16_t*)base)[idx]);
+  else if constexpr (ST == S_F32) return ((const float*)base)[idx];
+  else {
+    uint32_t e = ((const uint8_t*)base)[idx];
+    // 2^(e-127); e == 0 is the subnormal 2^-127, e == 255 is NaN.
+    return e == 0 ? __uint_as_float(0x00400000u) : (e == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e << 23));
+  }
+}
+
+// Output conversion (round to nearest even).
+template <int OF>
+__device__ __forceinline__ uint16_t f32_to_out(float v) {
+  if constexpr (OF == O_BF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// ---- 4-bit unpack ------------------------------------------------------------------
+// Magic-number decode: OR a nibble into the mantissa of 1.0.  bf16: 1 + u/128
+// (0x3F80 | u), f16: 1 + u/1024 (0x3C00 | u); both exact.  Dword q of the result holds
+// the nibbles at positions q (low half) and q+4 (high half) of the word.
+template <int AF>
+__device__ __forceinline__ u32x4 magic4(uint32_t w) {
+  constexpr uint32_t M = (AF == A_F16) ? 0x3C003C00u : 0x3F803F80u;
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) | M;
+  r[1] = ((w >> 4) & 0x000F000Fu) | M;
+  r[2] = ((w >> 8) & 0x000F000Fu) | M;
+  r[3] = ((w >> 12) & 0x000F000Fu) | M;
+  return r;
+}
+template <int AF> struct MagicConst;
+template <> struct MagicConst<A_BF16> { static constexpr float kInvStep = 128.0f; };
+template <> struct MagicConst<A_F16> { static constexpr float kInvStep = 1024.0f; };
+// fp8 activations on the 16-bit path are converted to bf16.
+template <> struct MagicConst<A_FP8> { static constexpr float kInvStep = 128.0f; };
+
+// e2m1 x 2^e -> 8 bf16 (natural order): one conversion per byte (two elements).
+template <int AF>
+__device__ __forceinline__ u32x4 fp4_to_16(uint32_t w, float scale) {
+  u32x4 r;
+  if constexpr (AF == A_F16) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  }
+  return r;
+}
+
+// int4 (two's complement, QUAD order) -> 8 e4m3 bytes in k order (2 dwords).
+// Table lookup with v_perm_b32: low 3 bits index one of two 8-entry tables
+// (q = 0..7 and q = -8..-1); bit 3 chooses between them through a byte mask built by
+// v_perm's constant selectors (12 -> 0x00, 13 -> 0xFF).  Every int4 value is an exact
+// e4m3 value, so the conversion is lossless.
+__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t x /* 4 nibbles, one per byte */) {
+  const uint32_t idx = x & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, idx);
+  const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, idx);
+  const uint32_t sel = ((x >> 3) & 0x01010101u) | 0x0C0C0C0Cu;
+  const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, sel);
+  return (neg & mask) | (pos & ~mask);
+}
+__device__ __forceinline__ u32x2 int4q_to_e4m3(uint32_t w) {
+  u32x2 r;
+  r[0] = int4x4_to_e4m3(w & 0x0F0F0F0Fu);          // positions 0,2,4,6 = elements 0..3
+  r[1] = int4x4_to_e4m3((w >> 4) & 0x0F0F0F0Fu);   // positions 1,3,5,7 = elements 4..7
+  return r;
+}
+
+// 8 consecutive e4m3 activations (2 dwords) -> 8 bf16 in the element order the QUAD
+// magic decode produces: (0,2) (4,6) (1,3) (5,7).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16_quad(uint32_t e0, uint32_t e1) {
+  const uint32_t g0 = __builtin_amdgcn_perm(e1, e0, 0x03010200u);  // f0 f2 f1 f3
+  const uint32_t g1 = __builtin_amdgcn_perm(e1, e0, 0x07050604u);  // f4 f6 f5 f7
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g0, 1.0f, false));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g0, 1.0f, true));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g1, 1.0f, true));
+  return r;
+}
+// 8 consecutive 16-bit activations (4 dwords, natural order) -> QUAD element order.
+__device__ __forceinline__ u32x4 a16_to_quad(u32x4 d) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);  // a0 a2
+  r[2] = __builtin_amdgcn_perm(d[1], d[0], 0x07060302u);  // a1 a3
+  r[1] = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);  // a4 a6
+  r[3] = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);  // a5 a7
+  return r;
+}
+
+// ---- MFMA wrappers -----------------------------------------------------------------
+template <int AF>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (AF == A_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// e4m3 x e4m3, 16x16x128 with neutral block scales (E8M0 127 = 1.0).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int AF>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (AF == A_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---- loads -------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+// Weight stream: read once, keep it out of the caches' way.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+}  // namespace qg

@@ -1,0 +1,55 @@
+// Host-visible launch interfaces of the device kernels (internal to libqg.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+// Arguments of the weight-streaming GEMM (dense and MoE).
+struct StreamArgs {
+  const uint8_t* w;          // prepared W region
+  const void* s;             // prepared S region
+  const uint32_t* z;         // prepared Z region or null
+  const void* x;             // activations [rows][k]
+  const float* x_scale;      // per-row scales for e4m3 activations
+  void* y;                   // output [rows][n]
+  int64_t m;                 // dense rows
+  int n, k, group;
+  int64_t w_expert_bytes;
+  const int32_t* sorted_ids; // MoE only
+  const int32_t* expert_ids;
+  const int32_t* num_post_pad;
+  int topk, sentinel;
+};
+
+struct StreamTile {
+  int mt, nt, kw, ch;        // row tiles (16 rows each), column tiles per wave, waves along K, chunk slots
+  unsigned grid_x, grid_y;
+};
+
+bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af, int of, int stype, bool zero,
+                        bool moe, hipStream_t st);
+
+// Weight transform kernels.
+struct RepackArgs {
+  const void* w; const void* s; const uint8_t* z;
+  uint8_t* out_w; uint8_t* out_s; uint32_t* out_z;
+  int experts, n, k, groups;
+  int w4;                    // 1: 4-bit codes, 0: e4m3 bytes
+  int order;                 // 0 natural, 1 pair, 2 quad
+  int bias8;                 // xor every nibble with 8
+  int s_bytes;               // bytes per scale element
+};
+void launch_repack(const RepackArgs& a, hipStream_t st);
+
+struct DequantArgs {
+  const uint8_t* w; const void* s; const uint32_t* z; float* out;
+  int n, k, groups, group, wp, af, stype, zero;
+};
+void launch_dequant(const DequantArgs& a, hipStream_t st);
+
+void launch_moe_align(const int32_t* ids, int tk, int experts, int block_m, int32_t* sorted_ids, int64_t cap_sorted,
+                      int32_t* expert_ids, int64_t cap_blocks, int32_t* num_post_pad, hipStream_t st);
+
+}  // namespace qg

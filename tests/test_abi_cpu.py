@@ -1,0 +1,127 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments on the host (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_gemm_amd as qg
+from quantized_gemm_amd import layers, synth
+from oracle import align as A
+from oracle import layout as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "qg.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qg_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qg.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(qg.EXPORTS)
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        assert qg.status_str(s)
+    assert qg.version() >> 16 == 1
+
+
+WORKLOADS = [
+    synth.dense_w4a16_sym_f16(m=1, n=64, k=256)[0],
+    synth.dense_w4a16_asym_bf16(m=1, n=64, k=512)[0],
+    synth.dense_w8a8_fp8(m=1, n=64, k=256)[0],
+    synth.moe_w4a16_mxfp4(t=2, experts=3, topk=2, n=64, k=256)[0],
+    synth.moe_w4a8_int4(t=2, experts=3, topk=2, n=64, k=256)[0],
+]
+
+
+@pytest.mark.parametrize("layer", WORKLOADS, ids=lambda l: l.name)
+def test_prepared_bytes_matches_layout_reference(layer):
+    d = layers.desc_for(layer)
+    sz = L.sizes(layer.w_type, layer.s_type, layer.n, layer.k, layer.group, layer.experts, layer.z is not None)
+    assert qg.prepared_bytes(d) == sz["total"]
+
+
+def _desc(**kw):
+    base = dict(w_type=qg.W_UINT4, s_type=qg.S_BF16, group_k=128, has_zero=1, a_type=qg.A_BF16,
+                compute=qg.C_NATIVE, out_type=qg.O_BF16, num_experts=1, n=512, k=1024)
+    base.update(kw)
+    return qg.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(n=100), dict(k=1000), dict(group_k=64), dict(has_zero=0), dict(s_type=qg.S_F32),
+                                dict(w_type=qg.W_INT4), dict(a_type=qg.A_FP8_E4M3),
+                                dict(w_type=qg.W_FP4_E2M1, s_type=qg.S_UE8M0, group_k=128, has_zero=0),
+                                dict(w_type=qg.W_FP8_E4M3, s_type=qg.S_F32, group_k=0, has_zero=0),
+                                dict(w_type=9), dict(n=-64), dict(out_type=qg.O_F16)])
+def test_invalid_or_unsupported_descriptions_have_no_size(kw):
+    assert qg.prepared_bytes(_desc(**kw)) == 0
+
+
+def test_prepare_rejects_before_touching_the_gpu():
+    lib = qg.lib()
+    p = qg.Prepared()
+    d = _desc()
+    st = lib.qg_prepare(ctypes.byref(d), None, None, None, None, 0, ctypes.byref(p), None)
+    assert st == 1  # null pointers
+    st = lib.qg_prepare(ctypes.byref(_desc(k=1000)), None, None, None, None, 0, ctypes.byref(p), None)
+    assert st == 2  # unsupported shape
+    fake = ctypes.c_void_p(4096)
+    st = lib.qg_prepare(ctypes.byref(d), fake, fake, fake, fake, 16, ctypes.byref(p), None)
+    assert st == 5  # output buffer too small
+
+
+def _forged(**kw):
+    p = qg.Prepared()
+    p.magic, p.layout_version, p.gfx_arch = qg.lib() and 0x31504751, 1, 950
+    p.desc = _desc()
+    p.dev = 4096
+    p.bytes = qg.prepared_bytes(p.desc)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_gemm_and_moe_reject_bad_handles_and_arguments():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.qg_gemm(None, fake, None, fake, 1, None, 0, None) == 1
+    assert lib.qg_gemm(ctypes.byref(_forged(magic=0)), fake, None, fake, 1, None, 0, None) == 4
+    assert lib.qg_gemm(ctypes.byref(_forged(layout_version=2)), fake, None, fake, 1, None, 0, None) == 4
+    assert lib.qg_gemm(ctypes.byref(_forged(gfx_arch=942)), fake, None, fake, 1, None, 0, None) == 3
+    assert lib.qg_gemm(ctypes.byref(_forged(bytes=16)), fake, None, fake, 1, None, 0, None) == 4
+    good = _forged()
+    assert lib.qg_gemm(ctypes.byref(good), fake, None, fake, -1, None, 0, None) == 1
+    assert lib.qg_gemm(ctypes.byref(good), fake, None, fake, 0, None, 0, None) == 0   # M == 0 is a no-op
+    assert lib.qg_gemm(ctypes.byref(good), None, None, fake, 4, None, 0, None) == 1
+    assert lib.qg_gemm(ctypes.byref(good), ctypes.c_void_p(4097), None, fake, 4, None, 0, None) == 1  # misaligned
+    assert lib.qg_moe_gemm(ctypes.byref(good), fake, None, fake, fake, fake, 0, 2, 16, fake, None, 0, None) == 0
+    assert lib.qg_moe_gemm(ctypes.byref(good), fake, None, fake, fake, fake, 4, 2, 48, fake, None, 0, None) == 2
+    assert lib.qg_dequant(ctypes.byref(good), 5, fake, None) == 1
+
+
+@pytest.mark.parametrize("t,topk,e,bm", [(1, 1, 128, 16), (16, 8, 128, 16), (4096, 8, 128, 64), (3, 2, 4, 2),
+                                         (8192, 6, 64, 64)])
+def test_capacity_matches_oracle(t, topk, e, bm):
+    assert qg.moe_capacity(t, topk, e, bm) == A.capacity(t, topk, e, bm)
+
+
+def test_moe_align_rejects_on_the_host():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.qg_moe_align(fake, 4, 2, 8, 12, fake, 100, fake, 10, fake, None) == 1   # block not a power of two
+    assert lib.qg_moe_align(fake, 4, 2, 8, 512, fake, 100, fake, 10, fake, None) == 1  # block too large
+    cs, cb = A.capacity(4, 2, 8, 4)
+    assert lib.qg_moe_align(fake, 4, 2, 8, 4, fake, cs - 1, fake, cb, fake, None) == 6
+    assert lib.qg_moe_align(fake, 4, 2, 8, 4, fake, cs, fake, cb - 1, fake, None) == 6
+    assert lib.qg_moe_align(fake, 4, 2, 1000, 4, fake, 10 ** 6, fake, 10 ** 6, fake, None) == 2
+    assert lib.qg_moe_align(None, 4, 2, 8, 4, fake, cs, fake, cb, fake, None) == 1

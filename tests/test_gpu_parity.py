@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bars: prepared bytes, read-back dequantization and MoE align are bit-exact;
+GEMM outputs satisfy max|Y - Y_ref| / max|Y_ref| <= 5e-3 for f16/bf16 activations and
+<= 2e-2 for e4m3 activations (Y_ref unrounded float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_amd as qg
+from quantized_gemm_amd import layers, synth
+from oracle import align as A
+from oracle import layout as L
+from oracle import reference as R
+
+pytestmark = pytest.mark.gpu
+
+TOL16 = 5e-3
+TOL8 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qg.lib()  # fail loudly if the HIP library is missing
+    yield
+
+
+def _tol(layer):
+    return TOL8 if layer.a_type == "e4m3" else TOL16
+
+
+SMALL = {
+    "c1": lambda s: synth.dense_w4a16_sym_f16(m=16, n=512, k=1024, seed=s),
+    "c2": lambda s: synth.dense_w4a16_asym_bf16(m=8, n=256, k=1024, seed=s),
+    "c3": lambda s: synth.dense_w8a8_fp8(m=8, n=128, k=512, seed=s),
+    "c4": lambda s: synth.moe_w4a16_mxfp4(t=8, experts=4, topk=2, n=128, k=512, seed=s),
+    "c5": lambda s: synth.moe_w4a8_int4(t=8, experts=3, topk=2, n=128, k=512, seed=s),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prepare_is_bit_exact(name):
+    layer, _ = SMALL[name](1)
+    p, buf = layers.prepare_layer(layer)
+    ref = L.repack(layer)
+    got = buf.cpu().numpy()
+    assert got.size == ref.size
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+    # deterministic: a second transform gives the same bytes
+    p2, buf2 = layers.prepare_layer(layer)
+    assert torch.equal(buf, buf2)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dequant_readback_is_bit_exact(name):
+    layer, _ = SMALL[name](2)
+    p, buf = layers.prepare_layer(layer)
+    for e in range(layer.experts):
+        out = torch.empty((layer.n, layer.k), dtype=torch.float32, device="cuda")
+        qg.dequant(p, e, out)
+        torch.cuda.synchronize()
+        ref = R.dequant_layer(layer, e)
+        if layer.w_type == "e4m3":
+            ref = ref.astype(np.float32)    # one correctly rounded product
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), np.asarray(ref, dtype=np.float64)), f"expert {e}"
+
+
+def _run_dense(layer, acts, m):
+    p, buf = layers.prepare_layer(layer)
+    x, xs = layers.acts_to_dev(acts)
+    y = torch.full((m, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
+    ws_n = qg.workspace_bytes(p, m)
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    qg.gemm(p, x, xs, y, m, ws)
+    torch.cuda.synchronize()
+    return layers.out_bits_to_f64(y)
+
+
+@pytest.mark.parametrize("m", [16])
+def test_dense_w4a16_sym_f16_full_size(m):
+    layer, acts = synth.dense_w4a16_sym_f16(m=m, n=512, k=1024, seed=0)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 15, 16, 17, 31, 33, 64, 100, 129])
+def test_dense_w4a16_asym_bf16_ragged_m(m):
+    layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=320, k=1280, seed=3)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("m", [1, 5, 64, 100])
+def test_dense_w8a8_fp8_ragged_m(m):
+    layer, acts = synth.dense_w8a8_fp8(m=m, n=192, k=768, seed=4)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
+
+
+@pytest.mark.parametrize("k", [256, 512, 9216])
+def test_dense_reduction_lengths(k):
+    # K below one wave's chunk budget and K beyond 64 chunks (several rounds per wave)
+    layer, acts = synth.dense_w4a16_asym_bf16(m=4, n=128, k=k, seed=5)
+    y = _run_dense(layer, acts, 4)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+def test_dense_is_deterministic():
+    layer, acts = synth.dense_w4a16_asym_bf16(m=16, n=256, k=1024, seed=6)
+    p, buf = layers.prepare_layer(layer)
+    x, _ = layers.acts_to_dev(acts)
+    y1 = torch.empty((16, 256), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    qg.gemm(p, x, None, y1, 16)
+    qg.gemm(p, x, None, y2, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ---- MoE ---------------------------------------------------------------------------------
+
+def _align_gpu(ids_np, experts, bm):
+    t, topk = ids_np.shape
+    cs, cb = qg.moe_capacity(t, topk, experts, bm)
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    s = torch.full((cs,), -7, dtype=torch.int32, device="cuda")
+    e = torch.full((cb,), -7, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    qg.moe_align(ids, t, topk, experts, bm, s, e, n)
+    torch.cuda.synchronize()
+    return s, e, n
+
+
+ALIGN_CASES = [
+    ("uniform", 64, 6, 64, 16), ("one_token", 1, 8, 128, 16), ("all_one_expert", 50, 1, 8, 16),
+    ("big_block", 300, 8, 128, 64), ("skewed", 1024, 6, 64, 32), ("tiny_block", 33, 3, 5, 1),
+    ("many", 8192, 6, 64, 64), ("invalid_ids", 40, 4, 16, 8),
+]
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES, ids=lambda c: c[0])
+def test_moe_align_is_bit_exact(case):
+    name, t, topk, experts, bm = case
+    rng = np.random.default_rng(t * 7 + topk)
+    if name == "all_one_expert":
+        ids = np.full((t, topk), 3, np.int32)
+    elif name == "skewed":
+        _, acts = synth.moe_w4a8_int4(t=t, experts=experts, topk=topk, n=64, k=256, seed=1)
+        ids = acts.topk_ids
+    else:
+        ids = np.stack([rng.permutation(experts)[:topk] for _ in range(t)]).astype(np.int32)
+    if name == "invalid_ids":
+        ids[0, 0] = -1
+        ids[5, 2] = experts
+    s, e, n = _align_gpu(ids, experts, bm)
+    rs, re_, rn = A.moe_align(ids, experts, bm)
+    assert int(n.item()) == rn
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(e.cpu().numpy(), re_)
+
+
+def _run_moe(layer, acts):
+    t, topk = acts.topk_ids.shape
+    p, buf = layers.prepare_layer(layer)
+    bm = qg.moe_block_m(p, t, topk)
+    s, e, n = _align_gpu(acts.topk_ids, layer.experts, bm)
+    x, xs = layers.acts_to_dev(acts)
+    y = torch.full((t * topk, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
+    qg.moe_gemm(p, x, xs, s, e, n, t, topk, bm, y)
+    torch.cuda.synchronize()
+    return layers.out_bits_to_f64(y).reshape(t, topk, layer.n)
+
+
+@pytest.mark.parametrize("t", [1, 5, 16, 40, 200])
+def test_moe_w4a16_mxfp4(t):
+    layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=8, topk=4, n=192, k=768, seed=t)
+    y = _run_moe(layer, acts)
+    ref = R.moe_reference(layer, acts)
+    assert R.relative_error(y, ref) <= TOL16
+
+
+@pytest.mark.parametrize("t", [1, 7, 64, 300])
+def test_moe_w4a8_int4_skewed(t):
+    layer, acts = synth.moe_w4a8_int4(t=t, experts=8, topk=3, n=128, k=1024, seed=t)
+    y = _run_moe(layer, acts)
+    ref = R.moe_reference(layer, acts)
+    assert R.relative_error(y, ref) <= TOL8
+
+
+def test_moe_dropped_slots_are_not_written():
+    layer, acts = synth.moe_w4a16_mxfp4(t=6, experts=4, topk=2, n=64, k=256, seed=9)
+    acts.topk_ids[2, 1] = -1
+    acts.topk_ids[4, 0] = 4
+    y = _run_moe(layer, acts)
+    assert np.all(np.isnan(y[2, 1])) and np.all(np.isnan(y[4, 0]))
+    ref = R.moe_reference(layer, acts)
+    ok = ~np.isnan(ref)
+    assert np.max(np.abs(y[ok] - ref[ok])) / np.max(np.abs(ref[ok])) <= TOL16
