@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized GEMM hot path on one MI355X.
+
+Default workload: dense W4A16 (uint4 codes, uint4 zero points, bf16 group-128 scales,
+bf16 activations), N = K = 8192, swept over M = 1, 16, 128, 1024, 4096.  One step runs
+qg_gemm once per M.  Inputs are resident in HBM before timing starts; the prepared
+weights are rotated over enough copies (>= 1 GiB in total) that every launch streams its
+weights from HBM rather than from the 256 MB last-level cache -- the pages time kernels
+with a cold L2.
+
+Output: one JSON line with the metric, whole-job throughput (TFLOP/s over the sweep),
+a per-M breakdown, the roofline of the dominant kernel (per-launch HIP-event
+durations) and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload dense_w4a16_asym_bf16|...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
+
+# Workloads: (builder, sweep, activation dtype tag for the MFMA peak, description)
+WORKLOADS = {
+    "dense_w4a16_asym_bf16": dict(sweep=[1, 16, 128, 1024, 4096], n=8192, k=8192, dtype="bf16",
+                                  desc="dense W4A16 uint4 + uint4 zero points, bf16 group-128 scales, "
+                                       "bf16 activations and output"),
+    "dense_w4a16_sym_f16": dict(sweep=[16], n=512, k=1024, dtype="f16",
+                                desc="dense W4A16 symmetric int4, f16 group-128 scales, f16 activations"),
+    "dense_w8a8_fp8": dict(sweep=[1, 64, 512, 4096], n=7168, k=7168, dtype="fp8",
+                           desc="dense W8A8 e4m3 per-channel x per-token scales, bf16 output"),
+}
+
+
+def weight_bytes(layer):
+    """Algorithmic weight bytes: packed codes + scales + zero points (4-bit packed)."""
+    bits = 8 if layer.w_type == "e4m3" else 4
+    g = 1 if layer.group == 0 else layer.k // layer.group
+    sb = {"f16": 2, "bf16": 2, "f32": 4, "ue8m0": 1}[layer.s_type]
+    b = layer.n * layer.k * bits // 8 + layer.n * g * sb
+    if layer.z is not None:
+        b += layer.n * g // 2
+    return b
+
+
+def cpu_baseline(builder, wl, budget_cols):
+    """The oracle, untuned, on a column slice of the same layer: all M of the sweep."""
+    from oracle import reference as R
+    import copy
+    layer, acts = builder(m=max(wl["sweep"]), n=wl["n"], k=wl["k"], seed=0)
+    sl = copy.copy(layer)
+    cols = np.arange(budget_cols)
+    x_all = R.activations(acts, layer.a_type)
+    t0 = time.perf_counter()
+    w = R.dequant_rows(layer, 0, cols)
+    flops = 0
+    for m in wl["sweep"]:
+        R.dense_gemm(x_all[:m], w)
+        flops += 2 * m * budget_cols * layer.k
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"float64 dequant + numpy.matmul of the first {budget_cols} of {layer.n} output columns, "
+                      f"every M of the sweep {wl['sweep']}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_w4a16_asym_bf16", choices=list(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-cols", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_gemm_amd as qg
+    from quantized_gemm_amd import layers, synth
+
+    wl = WORKLOADS[args.workload]
+    builder = getattr(synth, args.workload)
+    torch.cuda.set_device(0)
+    mmax = max(wl["sweep"])
+    layer, acts = builder(m=mmax, n=wl["n"], k=wl["k"], seed=0)
+    p0, buf0 = layers.prepare_layer(layer)
+    wbytes = weight_bytes(layer)
+    copies = args.copies or max(2, int(np.ceil((1 << 30) / buf0.numel())))
+    bufs, handles = [buf0], [p0]
+    for _ in range(copies - 1):
+        b = buf0.clone()
+        h = qg.Prepared.from_buffer_copy(p0)
+        h.dev = b.data_ptr()
+        bufs.append(b)
+        handles.append(h)
+    x_all, xs_all = layers.acts_to_dev(acts)
+    ys = {m: torch.empty((m, layer.n), dtype=layers.out_dtype(layer), device="cuda") for m in wl["sweep"]}
+    ws = {m: torch.zeros(max(1, qg.workspace_bytes(p0, m)), dtype=torch.uint8, device="cuda") for m in wl["sweep"]}
+    stream = torch.cuda.current_stream()
+
+    call = [0]
+
+    def one_step(events=None):
+        for i, m in enumerate(wl["sweep"]):
+            h = handles[call[0] % copies]
+            call[0] += 1
+            if events is not None:
+                events[i][0].record(stream)
+            qg.gemm(h, x_all[:m], None if xs_all is None else xs_all[:m], ys[m], m, ws[m])
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in wl["sweep"]]
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        one_step(ev[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    flops_step = sum(2 * m * layer.n * layer.k for m in wl["sweep"])
+    per_m = {}
+    for i, m in enumerate(wl["sweep"]):
+        d = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]) * 1e-3
+        avg = float(d.mean())
+        fl = 2 * m * layer.n * layer.k
+        per_m[str(m)] = {"us": round(avg * 1e6, 2), "us_median": round(float(np.median(d)) * 1e6, 2),
+                         "tflops": round(fl / avg / 1e12, 2), "weight_GBps": round(wbytes / avg / 1e9, 1),
+                         "hbm_frac": round(wbytes / avg / 1e9 / HBM_PEAK_GBPS, 4),
+                         "mfma_frac": round(fl / avg / 1e12 / MFMA_PEAK_TFLOPS[wl["dtype"]], 4)}
+    # dominant kernel = the launch with the largest average duration
+    dom = max(wl["sweep"], key=lambda m: per_m[str(m)]["us"])
+    dom_s = per_m[str(dom)]["us"] * 1e-6
+    dom_flops = 2 * dom * layer.n * layer.k
+    # the sweep's bound switches with M: weight bytes bound small M, the MFMA bounds large M
+    mfma_bound = dom_flops / (MFMA_PEAK_TFLOPS[wl["dtype"]] * 1e12) > wbytes / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(dom_flops / dom_s / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS[wl["dtype"]], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(wbytes / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = f"qg_gemm M={dom}"
+
+    result = {
+        "metric": "W4A16 qGEMM TFLOP/s + weight HBM GB/s (% roofline), M=1..4096, dense & MoE",
+        "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl["dtype"], "data": "synthetic",
+        "config": {"workload": wl["desc"], "n": layer.n, "k": layer.k, "m_sweep": wl["sweep"],
+                   "weight_bytes": wbytes, "weight_copies_rotated": copies},
+        "per_m": per_m,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(builder, wl, min(args.cpu_cols, layer.n))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

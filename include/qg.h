@@ -28,6 +28,10 @@
  * - QG_ERR_HIP is returned when a launch reports an error (hipGetLastError).
  * - M == 0 (or T == 0) is a successful no-op.
  * - Row-major tensors with contiguous rows; every pointer must be 16-byte aligned.
+ * - Workspaces: when qg_workspace_bytes() is non-zero the caller passes a device
+ *   buffer of at least that size whose bytes are ZERO before its first use (e.g.
+ *   allocated with a zero fill).  Every call leaves it ready for the next call; calls
+ *   that share one workspace must not run concurrently (use one per stream).
  * - Shape rules: n % 64 == 0, k % 256 == 0, k % group_k == 0.
  */
 #ifndef QG_H_

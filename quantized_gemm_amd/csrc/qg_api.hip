@@ -168,17 +168,32 @@ qg_status launched() {
 }
 
 // ---- M-bucket selector --------------------------------------------------------------
-// Weight-streaming family: one wave streams 2 column tiles (32 columns) of a chunk
-// range; KW waves share K inside a workgroup.
-StreamTile stream_tile(int64_t rows, int64_t n, int64_t k) {
+// Weight-streaming family: a workgroup of 2 column blocks x 4 K parts (4-bit weights)
+// or 1 x 8 (e4m3 weights) waves; rows in blocks of 16 / 32 / 64.
+StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
   StreamTile t{};
-  t.nt = 2;
-  t.ch = 8;
+  const bool w8 = w_type == QG_W_FP8_E4M3;
+  t.ncb = w8 ? 1 : 2;
+  t.kq = w8 ? 8 : 4;
   t.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  const int64_t nchunks = k / 128;
-  t.kw = nchunks >= 8 ? 8 : (nchunks >= 4 ? 4 : 2);   // K beyond 8*8 chunks runs in rounds
-  t.grid_x = (unsigned)(n / (16 * t.nt));
+  t.grid_x = (unsigned)((n / 16 + t.ncb - 1) / t.ncb);
   t.grid_y = (unsigned)((rows + 16 * t.mt - 1) / (16 * t.mt));
+  return t;
+}
+
+// MFMA-bound family: rows per tile 256 while that still leaves about 1.5 workgroups per
+// CU, else 128 (e4m3 weights always 128).
+constexpr int kCUs = 256;
+constexpr int64_t kStreamMaxRows = 64;
+
+bool has_mfma_path(const PathInfo& pi) { return pi.wp_small != WP_INT4Q_MAGIC; }
+
+MfmaTile mfma_tile(int64_t rows, int64_t n, int w_type) {
+  MfmaTile t{};
+  const int64_t ntiles = (n + 255) / 256;
+  t.bm = (w_type != QG_W_FP8_E4M3 && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
+  t.grid_x = (unsigned)(((rows + t.bm - 1) / t.bm) * ntiles);
+  t.grid_y = 1;
   return t;
 }
 
@@ -244,8 +259,8 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
 
 size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk) {
   (void)m_or_tokens; (void)topk;
-  if (check_prepared(p, nullptr) != QG_OK) return 0;
-  return 0;
+  (void)p;
+  return 0;   // no kernel of this version needs a workspace
 }
 
 static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
@@ -255,11 +270,21 @@ static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
   a.z = p->desc.has_zero ? (const uint32_t*)(base + p->off_z) : nullptr;
   a.n = (int)p->desc.n; a.k = (int)p->desc.k; a.group = p->desc.group_k;
   a.w_expert_bytes = (int64_t)p->w_expert_bytes;
+  a.s_bytes = (uint32_t)(p->s_expert_bytes * p->desc.num_experts);
+  a.z_bytes = (uint32_t)(p->z_expert_bytes * p->desc.num_experts);
+}
+
+// Buffer-resource limits of the kernels: every region a kernel addresses must stay
+// below 2^31 bytes (one expert's weights, all scales, the activations).
+bool fits_rsrc(const qg_prepared* p, int64_t x_rows) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t ab = p->desc.a_type == QG_A_FP8_E4M3 ? 1 : 2;
+  return (int64_t)p->w_expert_bytes < lim && (int64_t)(p->s_expert_bytes * p->desc.num_experts) < lim &&
+         (int64_t)(p->z_expert_bytes * p->desc.num_experts) < lim && x_rows * p->desc.k * ab < lim;
 }
 
 qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, void* y, int64_t m, void* ws,
                   size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   PathInfo pi;
   qg_status s = check_prepared(p, &pi);
   if (s != QG_OK) return s;
@@ -268,27 +293,39 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   if (m == 0) return QG_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return QG_ERR_INVALID_ARG;
   if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
-  if (m > (1 << 24)) return QG_ERR_UNSUPPORTED;
+  if (m > (1 << 24) || !fits_rsrc(p, m)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
+  (void)ws; (void)ws_bytes;
   StreamArgs a{};
   fill_stream_args(a, p);
-  a.x = x; a.x_scale = x_scale; a.y = y; a.m = m;
-  const StreamTile t = stream_tile(m, p->desc.n, p->desc.k);
-  QG_LOG("gemm m=%lld n=%lld k=%lld -> stream mt=%d nt=%d kw=%d grid=%ux%u", (long long)m, (long long)p->desc.n,
-         (long long)p->desc.k, t.mt, t.nt, t.kw, t.grid_x, t.grid_y);
+  a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
+  if (m > kStreamMaxRows && has_mfma_path(pi)) {
+    const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.w_type);
+    QG_LOG("gemm m=%lld n=%lld k=%lld -> mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
+           (long long)p->desc.k, t.bm, t.grid_x);
+    if (!launch_mfma_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
+      return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
+  const StreamTile t = stream_tile(m, p->desc.n, p->desc.w_type);
+  QG_LOG("gemm m=%lld n=%lld k=%lld -> stream mt=%d grid=%ux%u", (long long)m, (long long)p->desc.n,
+         (long long)p->desc.k, t.mt, t.grid_x, t.grid_y);
   if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();
 }
 
 int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
-  if (check_prepared(p, nullptr) != QG_OK || tokens < 0 || topk <= 0) return 0;
+  PathInfo pi;
+  if (check_prepared(p, &pi) != QG_OK || tokens < 0 || topk <= 0) return 0;
   const int64_t rows = tokens * topk;
   const int64_t per_expert = (rows + p->desc.num_experts - 1) / p->desc.num_experts;
   if (per_expert <= 16) return 16;
   if (per_expert <= 32) return 32;
-  return 64;
+  if (per_expert <= 96 || !has_mfma_path(pi)) return 64;
+  if (per_expert < 512 || p->desc.w_type == QG_W_FP8_E4M3) return 128;
+  return 256;
 }
 
 qg_status qg_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t block_m, int64_t* cap_sorted,
@@ -332,21 +369,33 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   if (!x || !y || !sorted_ids || !expert_ids || !num_post_pad || !aligned16(x) || !aligned16(y))
     return QG_ERR_INVALID_ARG;
   if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
-  if (block_m != 16 && block_m != 32 && block_m != 64) return QG_ERR_UNSUPPORTED;
-  if (tokens * topk > (int64_t)1 << 30) return QG_ERR_UNSUPPORTED;
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return QG_ERR_UNSUPPORTED;
+  if (block_m > kStreamMaxRows && !has_mfma_path(pi)) return QG_ERR_UNSUPPORTED;
+  if (block_m == 256 && p->desc.w_type == QG_W_FP8_E4M3) return QG_ERR_UNSUPPORTED;
+  if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
   int64_t cs, cb;
   qg_moe_capacity(tokens, topk, p->desc.num_experts, block_m, &cs, &cb);
   StreamArgs a{};
   fill_stream_args(a, p);
-  a.x = x; a.x_scale = x_scale; a.y = y; a.m = 0;
+  a.x = x; a.x_scale = x_scale; a.y = y; a.m = 0; a.x_rows = tokens;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.num_post_pad = num_post_pad;
   a.topk = topk; a.sentinel = (int)(tokens * topk);
-  StreamTile t = stream_tile(block_m, p->desc.n, p->desc.k);
+  if (block_m > kStreamMaxRows) {
+    MfmaTile t{};
+    t.bm = block_m;
+    t.grid_x = (unsigned)((p->desc.n + 255) / 256);
+    t.grid_y = (unsigned)cb;
+    QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> mfma grid=%ux%u", (long long)tokens, topk, block_m, t.grid_x, t.grid_y);
+    if (!launch_mfma_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
+      return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
+  StreamTile t = stream_tile(block_m, p->desc.n, p->desc.w_type);
   t.grid_y = (unsigned)cb;
-  QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> stream mt=%d kw=%d grid=%ux%u", (long long)tokens, topk, block_m, t.mt,
-         t.kw, t.grid_x, t.grid_y);
+  QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> stream mt=%d grid=%ux%u", (long long)tokens, topk, block_m, t.mt,
+         t.grid_x, t.grid_y);
   if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();

@@ -170,6 +170,23 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // ---- loads -------------------------------------------------------------------------
+// Raw buffer loads: an offset at or beyond the resource's size returns zeros without
+// touching memory, which keeps predicated loads branch-free (so the compiler can
+// count outstanding loads exactly and wait only for the ones an instruction needs).
+constexpr int kOOB = 0x7FFFFFF0;     // an offset past every resource this library builds
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);   // nt: streamed once
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 // Weight stream: read once, keep it out of the caches' way.
 __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {

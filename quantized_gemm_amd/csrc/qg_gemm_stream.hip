@@ -1,4 +1,4 @@
-// Dispatch of the weight-streaming GEMM to its per-format instantiation units.
+// Dispatch of the GEMM kernels to their per-format instantiation units.
 #include "qg_kernels.h"
 
 namespace qg {
@@ -14,6 +14,18 @@ bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af
   if (stream_int4q(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (stream_fp4(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (stream_fp8(a, t, wp, af, of, stype, zero, moe, st)) return true;
+  return false;
+}
+
+bool mfma_int4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
+bool mfma_fp4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
+bool mfma_fp8(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
+
+bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int stype, bool zero, bool moe,
+                      hipStream_t st) {
+  if (mfma_int4(a, t, wp, af, of, stype, zero, moe, st)) return true;
+  if (mfma_fp4(a, t, wp, af, of, stype, zero, moe, st)) return true;
+  if (mfma_fp8(a, t, wp, af, of, stype, zero, moe, st)) return true;
   return false;
 }
 

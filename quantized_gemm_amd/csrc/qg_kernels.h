@@ -15,6 +15,8 @@ struct StreamArgs {
   const float* x_scale;      // per-row scales for e4m3 activations
   void* y;                   // output [rows][n]
   int64_t m;                 // dense rows
+  int64_t x_rows;            // rows of x (dense: m, MoE: tokens)
+  uint32_t s_bytes, z_bytes; // sizes of the S / Z regions (all experts)
   int n, k, group;
   int64_t w_expert_bytes;
   const int32_t* sorted_ids; // MoE only
@@ -24,9 +26,19 @@ struct StreamArgs {
 };
 
 struct StreamTile {
-  int mt, nt, kw, ch;        // row tiles (16 rows each), column tiles per wave, waves along K, chunk slots
+  int mt;                    // row tiles of 16 rows per workgroup
+  int ncb, kq;               // 16-column blocks x K parts = waves per workgroup
   unsigned grid_x, grid_y;
 };
+
+// The MFMA-bound kernel takes the same arguments.
+typedef StreamArgs MfmaArgs;
+struct MfmaTile {
+  int bm;                    // rows per workgroup tile (128 or 256); 256 columns per tile
+  unsigned grid_x, grid_y;   // dense: grid_x = all tiles; MoE: grid_x = column tiles, grid_y = blocks
+};
+bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int stype, bool zero, bool moe,
+                      hipStream_t st);
 
 bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af, int of, int stype, bool zero,
                         bool moe, hipStream_t st);

@@ -5,9 +5,9 @@
 // strategies by input size; the wiki article ("Device and workload selection") says
 // the selector estimates where computation starts to dominate weight transfer.  At
 // small M every weight byte is used by exactly one wave, so this kernel streams the
-// prepared weights straight from HBM into VGPRs with 16-byte loads, issued for a whole
-// wave's share of K before any arithmetic (deep memory-level parallelism), and keeps
-// arithmetic per weight as low as possible:
+// prepared weights straight from HBM into VGPRs with 16-byte buffer loads, issued for
+// a wave's whole share (up to 16 KB) before any arithmetic, and keeps arithmetic per
+// weight low:
 //
 //  * int4/uint4 x f16/bf16: the nibble is ORed into the mantissa of 1.0 (exact operand
 //    1 + u/2^p, 7 VALU ops per 8 weights); the MFMA sums P = sum X*(1 + u/2^p) over
@@ -18,10 +18,13 @@
 //    conversion (exact).
 //  * e4m3 x e4m3: fp8 MFMA, per-token x per-channel scale in the epilogue.
 //
-// Grid: x = groups of 16*NT output columns, y = row blocks of 16*MT rows (dense) or MoE
-// blocks (rows gathered through sorted_ids).  A workgroup holds KW waves that split
-// K among themselves; partial sums are reduced through LDS at the end, so no
-// workspace, no atomics and a fixed summation order.
+// Work split inside a workgroup of NCB x KQ waves: wave (cb, q) owns 16-column block cb
+// and the q-th contiguous part of K.  Activations, scales and zero points for all parts
+// are staged in LDS in rounds (the next round's staging loads are in flight while the
+// current round computes); the KQ partial sums of a column block are added through LDS
+// in a fixed order at the end.  No workspace, no atomics, deterministic.
+// Grid: x = groups of NCB column blocks, y = row blocks of 16*MT rows (dense) or MoE
+// blocks (rows gathered through sorted_ids).
 #pragma once
 
 #include "qg_device.h"
@@ -29,262 +32,337 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NT, int KW, int CH, bool MOE>
-__global__ __launch_bounds__(64 * KW) void stream_gemm_kernel(StreamArgs a) {
-  constexpr int BM = 16 * MT;
-  constexpr int BN = 16 * NT;
-  constexpr bool kFp8Mfma = (WP == WP_FP8);
-  constexpr int ABYTES = (AF == A_FP8) ? 1 : 2;
-  // A lane supplies 32 consecutive k of each 128-wide chunk.
-  constexpr int A_U4 = 32 * ABYTES / 16;   // 16-byte pieces of activations per chunk and row tile
-  constexpr int B_U4 = kFp8Mfma ? 2 : 1;   // 16-byte weight units per chunk and column tile
+template <int WP, int AF>
+struct StreamTraits {
+  static constexpr bool kFp8Mfma = (WP == WP_FP8);
+  static constexpr int ABYTES = (AF == A_FP8) ? 1 : 2;
+  static constexpr int B_U4 = kFp8Mfma ? 2 : 1;       // 16-byte weight units per lane per chunk
+  // staged scale bytes per (column block, chunk): int4 paths 16 scales, fp4 4 groups x 16 bytes
+  static constexpr int SBYTES = (WP == WP_FP8) ? 0 : (WP == WP_FP4 ? 64 : 32);
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+// Chunks per wave whose weights are in flight at once (<= 16 KB per wave).
+template <int WP>
+constexpr int stream_max_chunks() { return WP == WP_FP8 ? 8 : 16; }
+
+// Chunks per K part staged per round: <= 64 KB of activations in LDS.
+template <int WP, int AF, int MT, int KQ>
+constexpr int stream_round_chunks() {
+  constexpr int per_chunk = 16 * MT * KQ * 128 * StreamTraits<WP, AF>::ABYTES;
+  constexpr int rc = (64 * 1024) / per_chunk;
+  return rc < 1 ? 1 : (rc > 16 ? 16 : rc);
+}
+
+template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NCB, int KQ, bool MOE>
+__global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a) {
+  using T = StreamTraits<WP, AF>;
+  constexpr int NW = NCB * KQ;
+  constexpr int NTHR = 64 * NW;
+  constexpr int BM = 16 * MT;
+  constexpr int RCR = stream_round_chunks<WP, AF, MT, KQ>();   // chunks per part per round
+  constexpr int CHMAX = stream_max_chunks<WP>();
+  constexpr int PART = RCR * 128 * T::ABYTES;                   // bytes of one part's round in an LDS row
+  constexpr int AROW = KQ * PART + 16;                          // padded LDS row (bytes)
+  constexpr int SB = T::SBYTES > 0 ? T::SBYTES : 16;
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * AROW];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[NCB * KQ * RCR * SB];
+  __shared__ __attribute__((aligned(8))) uint32_t sZ[NCB * KQ * RCR * 2];
+  __shared__ int sRowTok[BM];     // activation row of each tile row (-1: none)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cb = wave % NCB;            // column block of this wave within the workgroup
+  const int q = wave / NCB;             // K part of this wave
   const int r = lane & 15;
   const int g = lane >> 4;
 
-  // ---- which rows ----------------------------------------------------------------
+  // ---- rows of this block -----------------------------------------------------------
   int expert = 0;
-  int64_t rowbase = (int64_t)blockIdx.y * BM;
+  const int64_t rowbase = (int64_t)blockIdx.y * BM;
   if constexpr (MOE) {
     if (rowbase >= (int64_t)(*a.num_post_pad)) return;
     expert = a.expert_ids[blockIdx.y];
   }
-  // Row (activation index, output index) of this lane for each row tile.
-  int64_t arow[MT];
-  bool avalid[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t rr = rowbase + 16 * mt + r;
+  if (tid < BM) {
+    const int64_t rr = rowbase + tid;
+    int tok;
     if constexpr (MOE) {
       const int f = a.sorted_ids[rr];
-      avalid[mt] = f < a.sentinel;
-      arow[mt] = avalid[mt] ? (f / a.topk) : 0;
+      tok = f < a.sentinel ? f / a.topk : -1;
     } else {
-      avalid[mt] = rr < a.m;
-      arow[mt] = avalid[mt] ? rr : 0;
+      tok = rr < a.m ? (int)rr : -1;
     }
+    sRowTok[tid] = tok;
   }
 
-  const int nb0 = blockIdx.x * NT;      // first 16-column block
+  const int nb_count = a.n >> 4;
+  const int nbw = blockIdx.x * NCB + cb;                 // this wave's 16-column block
+  const bool wact = nbw < nb_count;                      // waves past N only help with staging
   const int nchunks = a.k >> 7;
-  const int per = (nchunks + KW - 1) / KW;
-  const int c0 = wave * per;
-  const int c1 = min(nchunks, c0 + per);
-  const int myc = max(0, c1 - c0);
+  const int per = (nchunks + KQ - 1) / KQ;               // chunks per K part
+  const int my0 = q * per;
+  const int myn = max(0, min(nchunks, my0 + per) - my0);
 
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
-  const int64_t kun = kFp8Mfma ? (a.k >> 4) : (a.k >> 5);  // units along K per 16-col block
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint8_t* xb = (const uint8_t*)a.x;
-  const int64_t xrow_bytes = (int64_t)a.k * ABYTES;
+  const int64_t kun = T::kFp8Mfma ? (a.k >> 4) : (a.k >> 5);   // 16-byte units along K per column block
   const int ngroups = a.group == 0 ? 1 : (a.k / a.group);
+  const int64_t xrow_bytes = (int64_t)a.k * T::ABYTES;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(a.x_rows * xrow_bytes));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)a.w_expert_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.s, a.s_bytes);
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, a.z_bytes);
 
-  // The wave's chunk range is processed in rounds of CH chunks; a round first issues
-  // all its weight loads, then consumes them.
-  for (int cb = 0; cb < myc; cb += CH) {
-  const int cnt = min(CH, myc - cb);
-  u32x4 bw[CH][NT][B_U4];
+  __syncthreads();   // sRowTok
+
+  // ---- staging of one round: activations, scales, zeros (registers first) --------------
+  constexpr int APR = KQ * PART / 16;                    // 16-byte pieces per activation row
+  constexpr int APIECES = BM * APR;
+  constexpr int AP_PER_T = (APIECES + NTHR - 1) / NTHR;
+  constexpr int SPPC = T::SBYTES / 16;                   // scale pieces per (block, part, chunk)
+  constexpr int SPIECES = NCB * KQ * RCR * SPPC;
+  constexpr int ZSLOTS = ZERO ? NCB * KQ * RCR : 0;
+  static_assert(SPIECES <= NTHR && ZSLOTS <= NTHR, "staging layout");
+
+  struct Stage {
+    u32x4 a[AP_PER_T];
+    u32x4 s;
+    u32x2 z;
+  };
+  auto load_stage = [&](int rnd, Stage& st) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    if (c < cnt) {
-      const int ch = c0 + cb + c;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int u = 0; u < B_U4; ++u) {
-          const int64_t ku = kFp8Mfma ? ((int64_t)ch * 8 + 2 * g + u) : ((int64_t)ch * 4 + g);
-          const uint8_t* p = wbase + ((((int64_t)(nb0 + t) * kun + ku) * 16 + r) << 4);
-          bw[c][t][u] = ldg16_stream(p);
-        }
+    for (int i = 0; i < AP_PER_T; ++i) {
+      const int p = tid + i * NTHR;
+      const int row = min(p / APR, BM - 1);
+      const int cp = p - (p / APR) * APR;                // piece within the row
+      const int pq = cp / (PART / 16);                   // K part of this piece
+      const int pc = cp - pq * (PART / 16);              // piece within that part's round
+      const int chunk_in_part = rnd * RCR + pc / (128 * T::ABYTES / 16);
+      const int tok = sRowTok[row];
+      const int pn = max(0, min(nchunks, pq * per + per) - pq * per);
+      const bool ok = p < APIECES && tok >= 0 && chunk_in_part < pn;
+      const int64_t off = (int64_t)tok * xrow_bytes + (int64_t)(pq * per + rnd * RCR) * 128 * T::ABYTES + 16 * pc;
+      st.a[i] = bload16(xr, ok ? (int)off : kOOB);
+    }
+    if constexpr (T::SBYTES > 0) {
+      const int slot = tid / SPPC, sq = tid - slot * SPPC;          // slot = (cb, part, chunk)
+      const int scb = slot / (KQ * RCR);
+      const int srem = slot - scb * KQ * RCR;
+      const int spq = srem / RCR, sc = srem - spq * RCR;
+      const int64_t nb = (int64_t)blockIdx.x * NCB + scb;
+      const int chunk_in_part = rnd * RCR + sc;
+      const int pn = max(0, min(nchunks, spq * per + per) - spq * per);
+      const int ch = spq * per + chunk_in_part;
+      const bool ok = tid < SPIECES && nb < nb_count && chunk_in_part < pn;
+      int64_t elem;
+      if constexpr (WP == WP_FP4) elem = (((int64_t)expert * nb_count + nb) * ngroups + (int64_t)ch * 4) * 16;
+      else elem = (((int64_t)expert * nb_count + nb) * ngroups + (a.group == 0 ? 0 : (ch * 128) / a.group)) * 16;
+      constexpr int EB = (ST == S_UE8M0) ? 1 : 2;
+      st.s = bload16(sr, ok ? (int)(elem * EB + 16 * sq) : kOOB);
+      if constexpr (ZERO) {
+        const int zcb = tid / (KQ * RCR);
+        const int zrem = tid - zcb * KQ * RCR;
+        const int zpq = zrem / RCR, zc = zrem - zpq * RCR;
+        const int64_t znb = (int64_t)blockIdx.x * NCB + zcb;
+        const int zcp = rnd * RCR + zc;
+        const int zpn = max(0, min(nchunks, zpq * per + per) - zpq * per);
+        const int zch = zpq * per + zcp;
+        const bool zok = tid < ZSLOTS && znb < nb_count && zcp < zpn;
+        const int grp = a.group == 0 ? 0 : (zch * 128) / a.group;
+        st.z = bload8(zr, zok ? (int)(((((int64_t)expert * nb_count + znb) * ngroups + grp) << 1) * 4) : kOOB);
       }
     }
-  }
-
+  };
+  auto store_stage = [&](const Stage& st) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    if (c < cnt) {
-      const int ch = c0 + cb + c;
-      // activations for this chunk
-      u32x4 av[MT][A_U4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint8_t* p = xb + arow[mt] * xrow_bytes + ((int64_t)ch * 128 + 32 * g) * ABYTES;
-#pragma unroll
-        for (int q = 0; q < A_U4; ++q)
-          av[mt][q] = avalid[mt] ? ldg16(p + 16 * q) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < AP_PER_T; ++i) {
+      const int p = tid + i * NTHR;
+      if (p < APIECES) {
+        const int row = p / APR, cp = p - row * APR;
+        *(u32x4*)(sA + row * AROW + 16 * cp) = st.a[i];
       }
+    }
+    if constexpr (T::SBYTES > 0) {
+      if (tid < SPIECES) *(u32x4*)(sS + 16 * tid) = st.s;
+      if constexpr (ZERO) {
+        if (tid < ZSLOTS) *(u32x2*)(sZ + 2 * tid) = st.z;
+      }
+    }
+  };
 
-      if constexpr (WP == WP_FP8) {
+  f32x4 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          i32x8 A;
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nrounds = (per + RCR - 1) / RCR;
+
+  // Weights: batches of CHMAX chunks of this wave's part, all loads of a batch in flight.
+  // The batch's first staging round is issued before its weights: load counters
+  // complete in order, so the first round can start as soon as its own data is in.
+  for (int b0 = 0; b0 < per; b0 += CHMAX) {
+    const int r0 = b0 / RCR, r1 = min(nrounds, (b0 + CHMAX) / RCR);
+    Stage st;
+    load_stage(r0, st);
+    u32x4 bw[CHMAX][T::B_U4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { A[q] = (int)av[mt][0][q]; A[4 + q] = (int)av[mt][1][q]; }
+    for (int c = 0; c < CHMAX; ++c) {
+      const int ch = my0 + b0 + c;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            i32x8 B;
+      for (int u = 0; u < T::B_U4; ++u) {
+        const int64_t ku = T::kFp8Mfma ? ((int64_t)ch * 8 + 2 * g + u) : ((int64_t)ch * 4 + g);
+        const bool ok = (b0 + c) < myn && wact;
+        bw[c][u] = bload16_stream(wr, ok ? (int)((((int64_t)nbw * kun + ku) * 16 + r) << 4) : kOOB);
+      }
+    }
+
+    // Rounds of this batch, unrolled so that every chunk's registers appear once.
 #pragma unroll
-            for (int q = 0; q < 4; ++q) { B[q] = (int)bw[c][t][0][q]; B[4 + q] = (int)bw[c][t][1][q]; }
-            acc[mt][t] = mfma16x16x128_fp8(A, B, acc[mt][t]);
-          }
-        }
-      } else if constexpr (WP == WP_FP4) {
-        // group 32 == one 16-byte unit: one scale per lane per chunk and column tile
+    for (int rr = 0; rr < CHMAX / RCR; ++rr) {
+      const int rnd = r0 + rr;
+      if (rnd < r1) {                                   // uniform over the workgroup
+        store_stage(st);
+        __syncthreads();
+        if (rnd + 1 < r1) load_stage(rnd + 1, st);     // next round in flight during this one
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int64_t sidx = (((int64_t)expert * (a.n >> 4) + nb0 + t) * ngroups + ((int64_t)ch * 4 + g)) * 16 + r;
-          const float sc = scale_to_f32<ST>(a.s, sidx);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 b = fp4_to_16<AF>(bw[c][t][0][j], sc);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              // piece j of the lane's 32 activations (16 bytes) pairs with word j of the unit
-              acc[mt][t] = mfma16x16x32<AF>(av[mt][j], b, acc[mt][t]);
-            }
-          }
-        }
-      } else {
-        // int4 / uint4 through the magic-number operand, promotion per chunk.
-        constexpr int MAF = (AF == A_FP8) ? A_BF16 : AF;   // fp8 activations run as bf16
-        constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
-        f32x4 P[MT][NT];
-        f32x4 R[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          R[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < NT; ++t) P[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        constexpr uint32_t ONE2 = (MAF == A_F16) ? 0x3C003C00u : 0x3F803F80u;
-        const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 aj[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if constexpr (AF == A_FP8) {
-              // 8 e4m3 = 2 dwords: piece j of 32 bytes -> av[mt][j>>1] dwords (j&1)*2, +1
-              const uint32_t e0 = av[mt][j >> 1][(j & 1) * 2 + 0];
-              const uint32_t e1 = av[mt][j >> 1][(j & 1) * 2 + 1];
-              aj[mt] = e4m3x8_to_bf16_quad(e0, e1);   // QUAD-ordered bf16
-            } else if constexpr (QUAD) {
-              aj[mt] = a16_to_quad(av[mt][j]);
+        for (int lc = 0; lc < RCR; ++lc) {
+          const int c = rr * RCR + lc;                  // chunk of the batch (compile-time)
+          if ((b0 + c) >= myn || !wact) continue;
+            const uint8_t* arow0 = sA + q * PART + lc * 128 * T::ABYTES;
+            const int slot = (cb * KQ + q) * RCR + lc;
+            if constexpr (WP == WP_FP8) {
+    #pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t* ap = arow0 + (16 * mt + r) * AROW + 32 * g;
+                const u32x4 a0 = *(const u32x4*)ap, a1 = *(const u32x4*)(ap + 16);
+                i32x8 A, B;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  A[i] = (int)a0[i]; A[4 + i] = (int)a1[i];
+                  B[i] = (int)bw[c][0][i]; B[4 + i] = (int)bw[c][1][i];
+                }
+                acc[mt] = mfma16x16x128_fp8(A, B, acc[mt]);
+              }
+            } else if constexpr (WP == WP_FP4) {
+              // group 32 == one 16-byte unit: the lane's scale is group 4*chunk + g
+              const uint32_t e8 = sS[slot * 64 + g * 16 + r];
+              const float sc = e8 == 0 ? __uint_as_float(0x00400000u)
+                                       : (e8 == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e8 << 23));
+    #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x4 b = fp4_to_16<AF>(bw[c][0][j], sc);
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                  const u32x4 av = *(const u32x4*)(arow0 + (16 * mt + r) * AROW + (32 * g + 8 * j) * 2);
+                  acc[mt] = mfma16x16x32<AF>(av, b, acc[mt]);
+                }
+              }
             } else {
-              aj[mt] = av[mt][j];
+              // int4 / uint4 through the magic-number operand, promotion per chunk.
+              constexpr int MAF = (AF == A_FP8) ? A_BF16 : AF;   // e4m3 activations run as bf16
+              constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
+              constexpr uint32_t ONE2 = (MAF == A_F16) ? 0x3C003C00u : 0x3F803F80u;
+              const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+              f32x4 P[MT], R[MT];
+    #pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+                P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                R[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+    #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                uint32_t wj = bw[c][0][j];
+                if constexpr (QUAD) wj ^= 0x88888888u;      // two's complement -> q + 8
+                const u32x4 b = magic4<MAF>(wj);
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                  u32x4 av;
+                  if constexpr (AF == A_FP8) {
+                    const u32x2 e = *(const u32x2*)(arow0 + (16 * mt + r) * AROW + 32 * g + 8 * j);
+                    av = e4m3x8_to_bf16_quad(e[0], e[1]);
+                  } else {
+                    av = *(const u32x4*)(arow0 + (16 * mt + r) * AROW + (32 * g + 8 * j) * 2);
+                    if constexpr (QUAD) av = a16_to_quad(av);
+                  }
+                  R[mt] = mfma16x16x32<MAF>(av, ones, R[mt]);
+                  P[mt] = mfma16x16x32<MAF>(av, b, P[mt]);
+                }
+              }
+              const uint32_t sbits = ((const uint16_t*)sS)[slot * 16 + r];
+              const float sp = (ST == S_F16 ? f16_bits_to_f32(sbits) : bf16_bits_to_f32(sbits)) *
+                               MagicConst<MAF>::kInvStep;
+              float zc;
+              if constexpr (ZERO) {
+                const uint32_t zw = sZ[slot * 2 + (r >> 3)];
+                zc = 1.0f + (float)((zw >> ((r & 7) * 4)) & 0xF) * (1.0f / MagicConst<MAF>::kInvStep);
+              } else {
+                zc = 1.0f + 8.0f * (1.0f / MagicConst<MAF>::kInvStep);
+              }
+    #pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(sp, __builtin_fmaf(-zc, R[mt][i], P[mt][i]), acc[mt][i]);
             }
-            R[mt] = mfma16x16x32<MAF>(aj[mt], ones, R[mt]);
-          }
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            uint32_t wj = bw[c][t][0][j];
-            if constexpr (QUAD) wj ^= 0x88888888u;     // two's complement -> q + 8
-            const u32x4 b = magic4<MAF>(wj);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) P[mt][t] = mfma16x16x32<MAF>(aj[mt], b, P[mt][t]);
-          }
         }
-        const int grp = a.group == 0 ? 0 : (ch * 128) / a.group;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int64_t sidx = (((int64_t)expert * (a.n >> 4) + nb0 + t) * ngroups + grp) * 16 + r;
-          const float sp = scale_to_f32<ST>(a.s, sidx) * MagicConst<MAF>::kInvStep;
-          float zc;
-          if constexpr (ZERO) {
-            const uint32_t zw = a.z[((((int64_t)expert * (a.n >> 4) + nb0 + t) * ngroups + grp) << 1) + (r >> 3)];
-            zc = 1.0f + (float)((zw >> ((r & 7) * 4)) & 0xF) * (1.0f / MagicConst<MAF>::kInvStep);
-          } else {
-            zc = 1.0f + 8.0f * (1.0f / MagicConst<MAF>::kInvStep);
-          }
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[mt][t][i] = __builtin_fmaf(sp, __builtin_fmaf(-zc, R[mt][i], P[mt][t][i]), acc[mt][t][i]);
-        }
+        __syncthreads();   // LDS is rewritten by the next round
       }
     }
   }
 
-  }  // rounds
-
-  // ---- reduce the KW partial sums through LDS and store --------------------------
-  __shared__ float red[KW][BM][BN + 1];
+  // ---- add the K parts through LDS (fixed order) and store ------------------------------
+  // (the activation buffer is free after the last round's barrier)
+  typedef float RedRow[NCB * 16 + 1];
+  static_assert(sizeof(float) * KQ * BM * (NCB * 16 + 1) <= sizeof(sA), "reduction buffer");
+  RedRow* sRed0 = reinterpret_cast<RedRow*>(sA);
+  auto sRed = [&](int p, int row) -> float* { return sRed0[p * BM + row]; };
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][16 * mt + 4 * g + i][16 * t + r] = acc[mt][t][i];
+    for (int i = 0; i < 4; ++i) sRed(q, 16 * mt + 4 * g + i)[16 * cb + r] = acc[mt][i];
   __syncthreads();
-
   uint16_t* yb = (uint16_t*)a.y;
-  for (int idx = threadIdx.x; idx < BM * BN; idx += 64 * KW) {
-    const int row = idx / BN;
-    const int col = idx - row * BN;
+  constexpr int BN = NCB * 16;
+  for (int idx = tid; idx < BM * BN; idx += NTHR) {
+    const int row = idx / BN, col = idx - row * BN;
+    const int tok = sRowTok[row];
+    const int64_t n = (int64_t)blockIdx.x * BN + col;
+    if (tok < 0 || n >= a.n) continue;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < KW; ++w) v += red[w][row][col];
-    const int64_t rr = rowbase + row;
-    int64_t orow, xrow;
-    bool ok;
-    if constexpr (MOE) {
-      const int f = a.sorted_ids[rr];
-      ok = f < a.sentinel;
-      orow = f;
-      xrow = ok ? f / a.topk : 0;
-    } else {
-      ok = rr < a.m;
-      orow = rr;
-      xrow = rr;
-    }
-    if (!ok) continue;
-    const int64_t n = (int64_t)nb0 * 16 + col;
-    if constexpr (AF == A_FP8) v *= a.x_scale[xrow];
+    for (int p = 0; p < KQ; ++p) v += sRed(p, row)[col];
     if constexpr (WP == WP_FP8) v *= ((const float*)a.s)[(int64_t)expert * a.n + n];
+    if constexpr (AF == A_FP8) v *= a.x_scale[tok];
+    int64_t orow;
+    if constexpr (MOE) orow = a.sorted_ids[rowbase + row];
+    else orow = rowbase + row;
     yb[orow * a.n + n] = f32_to_out<OF>(v);
   }
 }
 
-// ---- launch helpers (instantiated per weight path in qg_stream_*.hip) ------------
-template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NT, int KW, int CH, bool MOE>
-static void launch_one(const StreamArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((stream_gemm_kernel<WP, AF, OF, ST, ZERO, MT, NT, KW, CH, MOE>), grid, dim3(64 * KW), 0, st, a);
+// ---- launch helpers (instantiated per weight path in qg_stream_*.hip) --------------
+template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NCB, int KQ, bool MOE>
+static void launch_one(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
+  hipLaunchKernelGGL((stream_gemm_kernel<WP, AF, OF, ST, ZERO, MT, NCB, KQ, MOE>), dim3(t.grid_x, t.grid_y),
+                     dim3(64 * NCB * KQ), 0, st, a);
 }
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int NT, int KW, int CH, bool MOE>
-static bool launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t st) {
-  switch (mt) {
-    case 1: launch_one<WP, AF, OF, ST, ZERO, 1, NT, KW, CH, MOE>(a, grid, st); return true;
-    case 2: launch_one<WP, AF, OF, ST, ZERO, 2, NT, KW, CH, MOE>(a, grid, st); return true;
-    case 4: launch_one<WP, AF, OF, ST, ZERO, 4, NT, KW, CH, MOE>(a, grid, st); return true;
-    default: return false;
-  }
-}
-
+// Shapes: (NCB, KQ) = (2, 4) for 4-bit weights, (1, 8) for e4m3 weights.
 template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE>
-static bool launch_kw(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
-  dim3 grid(t.grid_x, t.grid_y);
-  if (t.nt != 2 || t.ch != 8) return false;
-  switch (t.kw) {
-    case 2: return launch_mt<WP, AF, OF, ST, ZERO, 2, 2, 8, MOE>(a, t.mt, grid, st);
-    case 4: return launch_mt<WP, AF, OF, ST, ZERO, 2, 4, 8, MOE>(a, t.mt, grid, st);
-    case 8: return launch_mt<WP, AF, OF, ST, ZERO, 2, 8, 8, MOE>(a, t.mt, grid, st);
+static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
+  constexpr int NCB = (WP == WP_FP8) ? 1 : 2;
+  constexpr int KQ = (WP == WP_FP8) ? 8 : 4;
+  if (t.ncb != NCB || t.kq != KQ) return false;
+  switch (t.mt) {
+    case 1: launch_one<WP, AF, OF, ST, ZERO, 1, NCB, KQ, MOE>(a, t, st); return true;
+    case 2: launch_one<WP, AF, OF, ST, ZERO, 2, NCB, KQ, MOE>(a, t, st); return true;
+    case 4: launch_one<WP, AF, OF, ST, ZERO, 4, NCB, KQ, MOE>(a, t, st); return true;
     default: return false;
   }
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
 static bool launch_stream_variant(const StreamArgs& a, const StreamTile& t, bool moe, hipStream_t st) {
-  return moe ? launch_kw<WP, AF, OF, ST, ZERO, true>(a, t, st) : launch_kw<WP, AF, OF, ST, ZERO, false>(a, t, st);
+  return moe ? launch_mt<WP, AF, OF, ST, ZERO, true>(a, t, st) : launch_mt<WP, AF, OF, ST, ZERO, false>(a, t, st);
 }
 
 }  // namespace qg

@@ -114,8 +114,9 @@ def test_dense_is_deterministic():
     x, _ = layers.acts_to_dev(acts)
     y1 = torch.empty((16, 256), dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty_like(y1)
-    qg.gemm(p, x, None, y1, 16)
-    qg.gemm(p, x, None, y2, 16)
+    ws = torch.zeros(max(1, qg.workspace_bytes(p, 16)), dtype=torch.uint8, device="cuda")
+    qg.gemm(p, x, None, y1, 16, ws)
+    qg.gemm(p, x, None, y2, 16, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
@@ -199,3 +200,41 @@ def test_moe_dropped_slots_are_not_written():
     ref = R.moe_reference(layer, acts)
     ok = ~np.isnan(ref)
     assert np.max(np.abs(y[ok] - ref[ok])) / np.max(np.abs(ref[ok])) <= TOL16
+
+
+# ---- the MFMA-bound path (row counts above the streaming bucket) ------------------------
+
+@pytest.mark.parametrize("m", [65, 128, 257, 600])
+def test_dense_w4a16_asym_bf16_mfma_path(m):
+    layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=320, k=1280, seed=7)   # 320: a partial 256-column tile
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("m", [100, 513])
+def test_dense_w4a16_sym_f16_mfma_path(m):
+    layer, acts = synth.dense_w4a16_sym_f16(m=m, n=512, k=1024, seed=8)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+def test_dense_mfma_tile_256_rows():
+    # enough row and column tiles for the 256-row tile (and the XCD remap of tile ids)
+    layer, acts = synth.dense_w4a16_asym_bf16(m=1536, n=2048, k=512, seed=9)
+    y = _run_dense(layer, acts, 1536)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("m", [65, 300])
+def test_dense_w8a8_fp8_mfma_path(m):
+    layer, acts = synth.dense_w8a8_fp8(m=m, n=320, k=768, seed=10)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
+
+
+@pytest.mark.parametrize("t,experts", [(400, 4), (1100, 4)])
+def test_moe_w4a16_mxfp4_mfma_path(t, experts):
+    # 200 and 550 rows per expert: blocks of 128 and 256 rows
+    layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=experts, topk=2, n=320, k=512, seed=11)
+    y = _run_moe(layer, acts)
+    assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL16
