@@ -89,6 +89,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-cols", type=int, default=8192)
+    ap.add_argument("--sweep", type=str, default="", help="comma-separated M values overriding the workload's sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -99,7 +100,9 @@ def main():
     import quantized_gemm_amd as qg
     from quantized_gemm_amd import layers, synth
 
-    wl = WORKLOADS[args.workload]
+    wl = dict(WORKLOADS[args.workload])
+    if args.sweep:
+        wl["sweep"] = [int(v) for v in args.sweep.split(",")]
     builder = getattr(synth, args.workload)
     torch.cuda.set_device(0)
     mmax = max(wl["sweep"])

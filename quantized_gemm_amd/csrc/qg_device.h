@@ -58,6 +58,20 @@ __device__ __forceinline__ float scale_to_f32(const void* base, int64_t idx) {
   }
 }
 
+// Two floats -> packed 16-bit pair (round to nearest even), low half = lo.
+template <int AF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (AF == A_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
 // Output conversion (round to nearest even).
 template <int OF>
 __device__ __forceinline__ uint16_t f32_to_out(float v) {

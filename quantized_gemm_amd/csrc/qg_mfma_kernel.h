@@ -10,10 +10,13 @@
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
 //     in the epilogue.
 //
-// Tile: BM x 256 per workgroup of 4 waves; wave w owns columns [64w, 64w+64) and all
-// BM rows (no weight is dequantized twice inside a workgroup).  Activations go through
+// Tile: BM x 256 per workgroup.  Four waves own the column quarters [64w, 64w+64); a
+// 128-row tile uses 4 waves (one per SIMD, no weight dequantized twice), a 256-row
+// tile uses 8 waves (two row halves, two waves per SIMD) so that one wave's dequant
+// VALU work co-executes with the other wave's MFMAs.  Activations go through
 // LDS, double-buffered, one 128-byte row segment per K step with a 16-byte XOR swizzle
-// (conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
+// by row bits 1..3 (16 consecutive rows read the same logical chunk from 16 distinct
+// banks groups: conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
 // prefetched two K steps ahead.  MFMA 32x32x16 (16-bit) or 32x32x64 (fp8), fp32
 // accumulation.  MoE: rows are gathered through sorted_ids and scattered on store.
 #pragma once
@@ -23,17 +26,19 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, int MW>
+__global__ __launch_bounds__(256 * MW) __attribute__((amdgpu_waves_per_eu(MW, MW)))
+void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (WP == WP_FP8);
   constexpr int AB = F8 ? 1 : 2;
   constexpr int BK = F8 ? 128 : 64;          // K per step; one LDS row segment = 128 bytes
-  constexpr int MT = BM / 32;                // 32-row MFMA tiles per wave
+  constexpr int NTHR = 256 * MW;             // MW groups of 4 waves split the rows
+  constexpr int MT = BM / 32 / MW;           // 32-row MFMA tiles per wave
   constexpr int NT = 2;                      // 32-column MFMA tiles per wave
   constexpr int BN = 256;
   constexpr int ROWB = 128;
   constexpr int STAGE = BM * ROWB;
-  constexpr int APT = STAGE / 16 / 256;      // 16-byte activation pieces per thread per step
+  constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
   constexpr int BU = F8 ? 4 : 1;             // 16-byte weight units per lane per tile and step
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2 * STAGE];
@@ -41,7 +46,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // column quarter
+  const int wm = __builtin_amdgcn_readfirstlane(tid >> 8);           // row part
   const int r = lane & 31;
   const int g = lane >> 5;
 
@@ -55,18 +61,24 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
     if (rowbase >= (int64_t)(*a.num_post_pad)) return;
     expert = a.expert_ids[blockIdx.y];
   } else {
-    // The dispatcher hands workgroups to the 8 XCDs round-robin (XCD = id % 8).  Tiles
-    // are numbered column-group-major and the id is remapped so that each XCD gets a
-    // contiguous run of tiles: the row tiles of one column group then share that XCD's
-    // L2 for their weight columns.
+    // The dispatcher hands workgroups to the 8 XCDs round-robin (XCD = id % 8).  When
+    // the column tiles split evenly, XCD x owns a contiguous band of column tiles and
+    // walks its row tiles row-major over that band, so the ~32 tiles it runs at once
+    // share a few activation row blocks and weight column blocks in its own L2.
     const int mtiles = (int)((a.m + BM - 1) / BM);
-    const int tiles = (int)gridDim.x;
-    int tile = blockIdx.x;
-    if ((tiles & 7) == 0) tile = (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3);
-    ntile = tile / mtiles;
-    rowbase = (int64_t)(tile - ntile * mtiles) * BM;
+    const int ntiles = (int)gridDim.x / mtiles;
+    const int id = blockIdx.x;
+    if ((ntiles & 7) == 0) {
+      const int nper = ntiles >> 3;
+      const int x = id & 7, l = id >> 3;
+      ntile = x * nper + l % nper;
+      rowbase = (int64_t)(l / nper) * BM;
+    } else {
+      ntile = id / mtiles;
+      rowbase = (int64_t)(id - ntile * mtiles) * BM;
+    }
   }
-  for (int i = tid; i < BM; i += 256) {
+  for (int i = tid; i < BM; i += NTHR) {
     const int64_t rr = rowbase + i;
     int tok;
     if constexpr (MOE) {
@@ -93,9 +105,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
   int a_off[APT];    // byte offset of the piece's source within a row-step, or -1
 #pragma unroll
   for (int i = 0; i < APT; ++i) {
-    const int p = tid + 256 * i;
+    const int p = tid + NTHR * i;
     const int row = p >> 3, pc = p & 7;
-    const int lc = pc ^ (row & 7);                         // logical 16-byte chunk
+    const int lc = pc ^ ((row >> 1) & 7);                  // logical 16-byte chunk
     const int tok = sRowTok[row];
     a_off[i] = tok < 0 ? -1 : (int)((int64_t)tok * xrow_bytes) + 16 * lc;
   }
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
   };
   auto store_a = [&](int buf, const u32x4* src) {
 #pragma unroll
-    for (int i = 0; i < APT; ++i) *(u32x4*)(sA + buf * STAGE + (tid + 256 * i) * 16) = src[i];
+    for (int i = 0; i < APT; ++i) *(u32x4*)(sA + buf * STAGE + (tid + NTHR * i) * 16) = src[i];
   };
 
   // ---- weights: per tile t, this lane's column and 16-byte units for a step ----------
@@ -176,13 +188,45 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
   load_b(1, b1);
   load_scale(1, sc1, zs1);
 
+  // Dequantize word j of this step's weights into the 16-bit MFMA operand of each tile.
+  auto dequant = [&](int j, const float* sc, const float* zs, u32x4 (&Bq)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t w = b0[t][0][j];
+      if constexpr (WP == WP_FP4) {
+        Bq[t] = fp4_to_16<AF>(w, sc[t]);
+      } else {
+        // PAIR nibble order: bytes of x0 hold elements (0,4,1,5), bytes of x1 (2,6,3,7).
+        // The empty asm hides where x0/x1 come from so that each byte converts with a
+        // single v_cvt_f32_ubyteN instead of a bit-field extract plus a conversion.
+        uint32_t x0 = w & 0x0F0F0F0Fu, x1 = (w >> 4) & 0x0F0F0F0Fu;
+        asm volatile("" : "+v"(x0), "+v"(x1));
+        const float e0 = __builtin_fmaf((float)(x0 & 0xFF), sc[t], zs[t]);
+        const float e4 = __builtin_fmaf((float)((x0 >> 8) & 0xFF), sc[t], zs[t]);
+        const float e1 = __builtin_fmaf((float)((x0 >> 16) & 0xFF), sc[t], zs[t]);
+        const float e5 = __builtin_fmaf((float)(x0 >> 24), sc[t], zs[t]);
+        const float e2 = __builtin_fmaf((float)(x1 & 0xFF), sc[t], zs[t]);
+        const float e6 = __builtin_fmaf((float)((x1 >> 8) & 0xFF), sc[t], zs[t]);
+        const float e3 = __builtin_fmaf((float)((x1 >> 16) & 0xFF), sc[t], zs[t]);
+        const float e7 = __builtin_fmaf((float)(x1 >> 24), sc[t], zs[t]);
+        Bq[t] = u32x4{pack2<AF>(e0, e1), pack2<AF>(e2, e3), pack2<AF>(e4, e5), pack2<AF>(e6, e7)};
+      }
+    }
+  };
+  // A fragments of 16-bit sub-step j (k = 32g + 8j of the step) for every row tile.
+  auto read_a16 = [&](const uint8_t* sAb, int j, u32x4 (&Af)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = 32 * (MT * wm + mt) + r;
+      Af[mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j) ^ ((row >> 1) & 7)));
+    }
+  };
+
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     __syncthreads();                                         // A(step) visible; other buffer free
-    if (step + 1 < nsteps) store_a(buf ^ 1, ast);
-    if (step + 2 < nsteps) load_a(step + 2, ast);
-    const float* sc = sc0;
-    const float* zs = zs0;
+    store_a(buf ^ 1, ast);                                   // A(step+1) (zeros past the end)
+    load_a(step + 2, ast);                                   // out-of-range steps read nothing
     const uint8_t* sAb = sA + buf * STAGE;
 
     if constexpr (F8) {
@@ -195,10 +239,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
           for (int i = 0; i < 4; ++i) { B[t][i] = (int)b0[t][2 * j][i]; B[t][4 + i] = (int)b0[t][2 * j + 1][i]; }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int row = 32 * mt + r;
+          const int row = 32 * (MT * wm + mt) + r;
           const int lc0 = 4 * g + 2 * j;
-          const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ (row & 7)));
-          const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ (row & 7)));
+          const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
+          const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
           i32x8 A;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
@@ -207,42 +251,21 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
         }
       }
     } else {
+      // Software pipeline over the 4 sub-steps: fragments and dequantized weights of
+      // sub-step j+1 are produced while the MFMAs of sub-step j run.
+      u32x4 Af[2][MT], Bq[2][NT];
+      read_a16(sAb, 0, Af[0]);
+      dequant(0, sc0, zs0, Bq[0]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x4 B[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t w = b0[t][0][j];
-          if constexpr (WP == WP_FP4) {
-            B[t] = fp4_to_16<AF>(w, sc[t]);
-          } else {
-            // PAIR nibble order: low bytes hold elements (0,4,1,5), high (2,6,3,7)
-            const uint32_t x0 = w & 0x0F0F0F0Fu, x1 = (w >> 4) & 0x0F0F0F0Fu;
-            float e[8];
-            e[0] = (float)(x0 & 0xFF); e[4] = (float)((x0 >> 8) & 0xFF);
-            e[1] = (float)((x0 >> 16) & 0xFF); e[5] = (float)(x0 >> 24);
-            e[2] = (float)(x1 & 0xFF); e[6] = (float)((x1 >> 8) & 0xFF);
-            e[3] = (float)((x1 >> 16) & 0xFF); e[7] = (float)(x1 >> 24);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = __builtin_fmaf(e[i], sc[t], zs[t]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if constexpr (AF == A_F16) {
-                B[t][i] = (uint32_t)f32_to_out<O_F16>(e[2 * i]) | ((uint32_t)f32_to_out<O_F16>(e[2 * i + 1]) << 16);
-              } else {
-                B[t][i] = (uint32_t)f32_to_out<O_BF16>(e[2 * i]) | ((uint32_t)f32_to_out<O_BF16>(e[2 * i + 1]) << 16);
-              }
-            }
-          }
+        if (j + 1 < 4) {
+          read_a16(sAb, j + 1, Af[(j + 1) & 1]);
+          dequant(j + 1, sc0, zs0, Bq[(j + 1) & 1]);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int row = 32 * mt + r;
-          const int lc = 4 * g + j;
-          const u32x4 av = *(const u32x4*)(sAb + row * ROWB + 16 * (lc ^ (row & 7)));
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(av, B[t], acc[mt][t]);
-        }
+          for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[j & 1][mt], Bq[j & 1][t], acc[mt][t]);
       }
     }
     // rotate the weight and scale prefetch
@@ -253,10 +276,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
       sc0[t] = sc1[t];
       zs0[t] = zs1[t];
     }
-    if (step + 2 < nsteps) {
-      load_b(step + 2, b1);
-      load_scale(step + 2, sc1, zs1);
-    }
+    load_b(step + 2, b1);
+    load_scale(min(step + 2, nsteps - 1), sc1, zs1);
   }
 
   // ---- epilogue: lane (r, g) of a 32x32 tile holds column r, rows 8*(i/4) + 4*g + i%4 ----
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
+        const int row = 32 * (MT * wm + mt) + 8 * (i >> 2) + 4 * g + (i & 3);
         const int tok = sRowTok[row];
         if (tok < 0) continue;
         float v = acc[mt][t][i] * sw;
@@ -286,7 +307,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
 
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE>), grid, dim3(256), 0, st, a);
+  // 256-row tiles run as 8 waves (2 row halves x 4 column quarters, 2 waves per SIMD)
+  constexpr int MW = BM == 256 ? 2 : 1;
+  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, MW>), grid, dim3(256 * MW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
