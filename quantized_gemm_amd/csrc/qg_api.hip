@@ -56,6 +56,7 @@ int current_arch() {
 // Which kernel weight path a layer uses.
 struct PathInfo {
   int wp_small;   // path of the weight-streaming kernel
+  int wp_mfma;    // path of the MFMA-bound kernel
   int order;      // repack nibble order: 0 natural, 1 pair, 2 quad
   int bias8;      // repack stores q + 8
   int w4;         // 4-bit codes
@@ -121,6 +122,7 @@ qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
       return QG_ERR_UNSUPPORTED;
     p.wp_small = WP_FP8; p.w4 = 0; p.af = A_FP8; p.st = S_F32; p.dq_wp = WP_FP8;
   }
+  p.wp_mfma = p.wp_small == WP_INT4Q_MAGIC ? WP_INT4Q_FP8 : p.wp_small;
   if (pi) *pi = p;
   return QG_OK;
 }
@@ -186,12 +188,13 @@ StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
 constexpr int kCUs = 256;
 constexpr int64_t kStreamMaxRows = 64;
 
-bool has_mfma_path(const PathInfo& pi) { return pi.wp_small != WP_INT4Q_MAGIC; }
+// e4m3 weights and the int4 -> e4m3 path use 128-row tiles only.
+bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8 && pi.wp_mfma != WP_INT4Q_FP8; }
 
-MfmaTile mfma_tile(int64_t rows, int64_t n, int w_type) {
+MfmaTile mfma_tile(int64_t rows, int64_t n, const PathInfo& pi) {
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
-  t.bm = (w_type != QG_W_FP8_E4M3 && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
+  t.bm = (mfma_rows256(pi) && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
   t.grid_x = (unsigned)(((rows + t.bm - 1) / t.bm) * ntiles);
   t.grid_y = 1;
   return t;
@@ -300,11 +303,11 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   StreamArgs a{};
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
-  if (m > kStreamMaxRows && has_mfma_path(pi)) {
-    const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.w_type);
+  if (m > kStreamMaxRows) {
+    const MfmaTile t = mfma_tile(m, p->desc.n, pi);
     QG_LOG("gemm m=%lld n=%lld k=%lld -> mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
            (long long)p->desc.k, t.bm, t.grid_x);
-    if (!launch_mfma_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
+    if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
       return QG_ERR_UNSUPPORTED;
     return launched();
   }
@@ -323,8 +326,8 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   const int64_t per_expert = (rows + p->desc.num_experts - 1) / p->desc.num_experts;
   if (per_expert <= 16) return 16;
   if (per_expert <= 32) return 32;
-  if (per_expert <= 96 || !has_mfma_path(pi)) return 64;
-  if (per_expert < 512 || p->desc.w_type == QG_W_FP8_E4M3) return 128;
+  if (per_expert <= 96) return 64;
+  if (per_expert < 512 || !mfma_rows256(pi)) return 128;
   return 256;
 }
 
@@ -370,8 +373,7 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     return QG_ERR_INVALID_ARG;
   if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
   if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return QG_ERR_UNSUPPORTED;
-  if (block_m > kStreamMaxRows && !has_mfma_path(pi)) return QG_ERR_UNSUPPORTED;
-  if (block_m == 256 && p->desc.w_type == QG_W_FP8_E4M3) return QG_ERR_UNSUPPORTED;
+  if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
@@ -388,7 +390,7 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     t.grid_x = (unsigned)((p->desc.n + 255) / 256);
     t.grid_y = (unsigned)cb;
     QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> mfma grid=%ux%u", (long long)tokens, topk, block_m, t.grid_x, t.grid_y);
-    if (!launch_mfma_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
+    if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
       return QG_ERR_UNSUPPORTED;
     return launched();
   }

@@ -20,12 +20,14 @@ bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af
 bool mfma_int4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 bool mfma_fp4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 bool mfma_fp8(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
+bool mfma_w4a8(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 
 bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int stype, bool zero, bool moe,
                       hipStream_t st) {
   if (mfma_int4(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (mfma_fp4(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (mfma_fp8(a, t, wp, af, of, stype, zero, moe, st)) return true;
+  if (mfma_w4a8(a, t, wp, af, of, stype, zero, moe, st)) return true;
   return false;
 }
 

@@ -238,3 +238,20 @@ def test_moe_w4a16_mxfp4_mfma_path(t, experts):
     layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=experts, topk=2, n=320, k=512, seed=11)
     y = _run_moe(layer, acts)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("m", [8, 100, 300])
+def test_dense_w4a8_int4_to_fp8(m):
+    # the W4A8 layer used densely (one expert): streaming path at 8 rows, fp8 MFMA with
+    # per-group promotion above 64 rows
+    layer, acts = synth.moe_w4a8_int4(t=m, experts=1, topk=1, n=320, k=1024, seed=12)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
+
+
+@pytest.mark.parametrize("t", [400, 1000])
+def test_moe_w4a8_int4_mfma_path(t):
+    # 200 / 500 rows per expert (skewed router): blocks of 128 rows on the fp8 MFMA kernel
+    layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=13)
+    y = _run_moe(layer, acts)
+    assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
