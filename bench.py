@@ -43,11 +43,17 @@ WORKLOADS = {
                                 desc="dense W4A16 symmetric int4, f16 group-128 scales, f16 activations"),
     "dense_w8a8_fp8": dict(sweep=[1, 64, 512, 4096], n=7168, k=7168, dtype="fp8",
                            desc="dense W8A8 e4m3 per-channel x per-token scales, bf16 output"),
+    "moe_w4a16_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="bf16", moe=dict(experts=128, topk=8),
+                            desc="MoE W4A16 MXFP4 (e2m1 + UE8M0/32), E=128 top-8, fused gate+up N=4096, K=7168, "
+                                 "bf16 activations; T sweep"),
+    "moe_w4a8_int4": dict(sweep=[64, 1024, 8192], n=2816, k=4096, dtype="fp8", moe=dict(experts=64, topk=6),
+                          desc="MoE W4A8 int4 -> e4m3 in-kernel, bf16 group-128 scales, E=64 top-6, N=2816, K=4096, "
+                               "per-token e4m3 activations, 20% of tokens biased to 4 hot experts; T sweep"),
 }
 
 
 def weight_bytes(layer):
-    """Algorithmic weight bytes: packed codes + scales + zero points (4-bit packed)."""
+    """Algorithmic weight bytes of ONE expert: packed codes + scales + zero points (4-bit packed)."""
     bits = 8 if layer.w_type == "e4m3" else 4
     g = 1 if layer.group == 0 else layer.k // layer.group
     sb = {"f16": 2, "bf16": 2, "f32": 4, "ue8m0": 1}[layer.s_type]
@@ -150,9 +156,22 @@ def main():
     builder = getattr(synth, args.workload)
     torch.cuda.set_device(0)
     mmax = max(wl["sweep"])
-    layer, acts = builder(m=mmax, n=wl["n"], k=wl["k"], seed=0)
+    moe = wl.get("moe")
+    if moe:
+        layer, acts = builder(t=mmax, n=wl["n"], k=wl["k"], seed=0, **moe)
+    else:
+        layer, acts = builder(m=mmax, n=wl["n"], k=wl["k"], seed=0)
     p0, buf0 = layers.prepare_layer(layer)
-    wbytes = weight_bytes(layer)
+    wbytes_expert = weight_bytes(layer)
+    # weight bytes a launch must stream: the dense layer, or the experts the first m tokens touch
+    wbytes_of = {}
+    for m in wl["sweep"]:
+        if moe:
+            touched = len(np.unique(acts.topk_ids[:m]))
+            wbytes_of[m] = touched * wbytes_expert
+        else:
+            wbytes_of[m] = wbytes_expert
+    wbytes = wbytes_expert
     copies = args.copies or max(2, int(np.ceil((1 << 30) / buf0.numel())))
     bufs, handles = [buf0], [p0]
     for _ in range(copies - 1):
@@ -162,9 +181,20 @@ def main():
         bufs.append(b)
         handles.append(h)
     x_all, xs_all = layers.acts_to_dev(acts)
-    ys = {m: torch.empty((m, layer.n), dtype=layers.out_dtype(layer), device="cuda") for m in wl["sweep"]}
-    ws = {m: torch.zeros(max(1, qg.workspace_bytes(p0, m)), dtype=torch.uint8, device="cuda") for m in wl["sweep"]}
+    rows_of = {m: m * (moe["topk"] if moe else 1) for m in wl["sweep"]}
+    ys = {m: torch.empty((rows_of[m], layer.n), dtype=layers.out_dtype(layer), device="cuda") for m in wl["sweep"]}
+    ws = {m: torch.zeros(max(1, qg.workspace_bytes(p0, m, moe["topk"] if moe else 0)), dtype=torch.uint8,
+                         device="cuda") for m in wl["sweep"]}
     stream = torch.cuda.current_stream()
+    align = {}
+    if moe:
+        ids_all = torch.from_numpy(np.ascontiguousarray(acts.topk_ids)).cuda()
+        for m in wl["sweep"]:
+            bm = qg.moe_block_m(p0, m, moe["topk"])
+            cs, cb = qg.moe_capacity(m, moe["topk"], moe["experts"], bm)
+            align[m] = (bm, torch.empty(cs, dtype=torch.int32, device="cuda"),
+                        torch.empty(cb, dtype=torch.int32, device="cuda"), torch.empty(1, dtype=torch.int32, device="cuda"),
+                        ids_all[:m].contiguous())
 
     call = [0]
 
@@ -172,9 +202,19 @@ def main():
         for i, m in enumerate(wl["sweep"]):
             h = handles[call[0] % copies]
             call[0] += 1
-            if events is not None:
-                events[i][0].record(stream)
-            qg.gemm(h, x_all[:m], None if xs_all is None else xs_all[:m], ys[m], m, ws[m])
+            xs = None if xs_all is None else xs_all[:m]
+            if moe:
+                bm, sid, eid, npp, ids = align[m]
+                if events is not None:
+                    events[i][2].record(stream)
+                qg.moe_align(ids, m, moe["topk"], moe["experts"], bm, sid, eid, npp)
+                if events is not None:
+                    events[i][0].record(stream)
+                qg.moe_gemm(h, x_all[:m], xs, sid, eid, npp, m, moe["topk"], bm, ys[m], ws[m])
+            else:
+                if events is not None:
+                    events[i][0].record(stream)
+                qg.gemm(h, x_all[:m], xs, ys[m], m, ws[m])
             if events is not None:
                 events[i][1].record(stream)
 
@@ -182,7 +222,7 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in wl["sweep"]]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in wl["sweep"]]
           for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -194,30 +234,36 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    flops_step = sum(2 * m * layer.n * layer.k for m in wl["sweep"])
+    flops_step = sum(2 * rows_of[m] * layer.n * layer.k for m in wl["sweep"])
     per_m = {}
     for i, m in enumerate(wl["sweep"]):
         d = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]) * 1e-3
         avg = float(d.mean())
-        fl = 2 * m * layer.n * layer.k
+        fl = 2 * rows_of[m] * layer.n * layer.k
+        wb = wbytes_of[m]
         per_m[str(m)] = {"us": round(avg * 1e6, 2), "us_median": round(float(np.median(d)) * 1e6, 2),
-                         "tflops": round(fl / avg / 1e12, 2), "weight_GBps": round(wbytes / avg / 1e9, 1),
-                         "hbm_frac": round(wbytes / avg / 1e9 / HBM_PEAK_GBPS, 4),
+                         "tflops": round(fl / avg / 1e12, 2), "weight_GBps": round(wb / avg / 1e9, 1),
+                         "hbm_frac": round(wb / avg / 1e9 / HBM_PEAK_GBPS, 4),
                          "mfma_frac": round(fl / avg / 1e12 / MFMA_PEAK_TFLOPS[wl["dtype"]], 4)}
+        if moe:
+            da = np.array([ev[s][i][2].elapsed_time(ev[s][i][0]) for s in range(args.steps)]) * 1e-3
+            per_m[str(m)]["align_us"] = round(float(da.mean()) * 1e6, 2)
+            per_m[str(m)]["weight_bytes"] = wb
     # dominant kernel = the launch with the largest average duration
     dom = max(wl["sweep"], key=lambda m: per_m[str(m)]["us"])
     dom_s = per_m[str(dom)]["us"] * 1e-6
-    dom_flops = 2 * dom * layer.n * layer.k
+    dom_flops = 2 * rows_of[dom] * layer.n * layer.k
     # the sweep's bound switches with M: weight bytes bound small M, the MFMA bounds large M
-    mfma_bound = dom_flops / (MFMA_PEAK_TFLOPS[wl["dtype"]] * 1e12) > wbytes / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = dom_flops / (MFMA_PEAK_TFLOPS[wl["dtype"]] * 1e12) > wbytes_of[dom] / (HBM_PEAK_GBPS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(dom_flops / dom_s / 1e12, 2),
                 "peak": MFMA_PEAK_TFLOPS[wl["dtype"]], "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "hbm", "achieved": round(wbytes / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": round(wbytes_of[dom] / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(args.workload, dom) if mfma_bound else None
-    roof["kernel"] = f"qg_gemm M={dom}"
+    roof["kernel"] = f"{'qg_moe_gemm T' if moe else 'qg_gemm M'}={dom}"
 
     result = {
         "metric": "W4A16 qGEMM TFLOP/s + weight HBM GB/s (% roofline), M=1..4096, dense & MoE",
@@ -228,11 +274,11 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl["dtype"], "data": "synthetic",
         "config": {"workload": wl["desc"], "n": layer.n, "k": layer.k, "m_sweep": wl["sweep"],
-                   "weight_bytes": wbytes, "weight_copies_rotated": copies},
+                   "weight_bytes": wbytes * layer.experts, "weight_copies_rotated": copies},
         "per_m": per_m,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not moe:
         result["cpu_baseline"] = cpu_baseline(builder, wl, min(args.cpu_cols, layer.n))
     print(json.dumps(result), flush=True)
 

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import ctypes
 import os
 import shutil
 import subprocess
@@ -58,6 +59,12 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # Resolve every symbol now: a kernel template whose host stub was not emitted links
+    # fine but fails to load.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")

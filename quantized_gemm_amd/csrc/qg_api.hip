@@ -195,6 +195,9 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, const PathInfo& pi) {
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
   t.bm = (mfma_rows256(pi) && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
+  // experiment-only override of the row tile (QG_MFMA_BM=128|256)
+  static const char* ov = getenv("QG_MFMA_BM");
+  if (ov && mfma_rows256(pi) && (atoi(ov) == 128 || atoi(ov) == 256)) t.bm = atoi(ov);
   t.grid_x = (unsigned)(((rows + t.bm - 1) / t.bm) * ntiles);
   t.grid_y = 1;
   return t;

@@ -197,6 +197,12 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);   // nt: streamed once
 }
+// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l (lds is
+// wave-uniform); an out-of-range offset stores zeros.  Kept out of kernel templates: used
+// there directly, the host pass drops the templates' launch stubs.
+__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }

@@ -26,8 +26,8 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, int MW>
-__global__ __launch_bounds__(256 * MW) __attribute__((amdgpu_waves_per_eu(MW, MW)))
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, int MW, int OCC>
+__global__ __launch_bounds__(256 * MW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (WP == WP_FP8);
   constexpr int AB = F8 ? 1 : 2;
@@ -38,10 +38,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int BN = 256;
   constexpr int ROWB = 128;
   constexpr int STAGE = BM * ROWB;
+  constexpr int NS = 3;                      // activation stages in LDS (ring)
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
   constexpr int BU = F8 ? 4 : 1;             // 16-byte weight units per lane per tile and step
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2 * STAGE];
+  // one array per stage: the compiler then sees which stage an LDS read and an
+  // HBM->LDS load touch, and waits only where they really overlap
+  __shared__ __attribute__((aligned(16))) uint8_t sA0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sA1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sA2[STAGE];
   __shared__ int sRowTok[BM];
 
   const int tid = threadIdx.x;
@@ -111,14 +116,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
     const int tok = sRowTok[row];
     a_off[i] = tok < 0 ? -1 : (int)((int64_t)tok * xrow_bytes) + 16 * lc;
   }
-  auto load_a = [&](int step, u32x4* dst) {
+  // Activations go HBM -> LDS directly (buffer_load ... lds): lane l of a wave writes the
+  // 16 bytes at the wave's LDS base + 16 l, so piece p = tid + NTHR*i lands in slot p of the
+  // stage.  Rows without a token and steps past the end read out of range, which stores
+  // zeros.  Exactly APT loads per thread per step, no branches (the wait counts rely on it).
+  const int wave_slot = (tid & ~63) * 16;
+  auto issue_a = [&](int step, uint8_t* stage) {
 #pragma unroll
     for (int i = 0; i < APT; ++i)
-      dst[i] = bload16(xr, a_off[i] < 0 ? kOOB : a_off[i] + step * ROWB);
-  };
-  auto store_a = [&](int buf, const u32x4* src) {
-#pragma unroll
-    for (int i = 0; i < APT; ++i) *(u32x4*)(sA + buf * STAGE + (tid + NTHR * i) * 16) = src[i];
+      bload16_lds(xr, stage + NTHR * 16 * i + wave_slot, a_off[i] < 0 || step >= nsteps ? kOOB : a_off[i] + step * ROWB);
   };
 
   // ---- weights: per tile t, this lane's column and 16-byte units for a step ----------
@@ -176,23 +182,32 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][t][i] = 0.f;
 
-  // ---- prologue: A(0) -> LDS, A(1) in registers, B and scales of steps 0 and 1 ------
-  u32x4 ast[APT];
+  // ---- prologue: A(0), A(1) -> LDS stages 0, 1; weights and scales of steps 0 and 1 --
+  // Vector-memory issue order, kept by sched_barrier: A(0) B(0) A(1) B(1), then per step s
+  // A(s+2) at the top and B(s+2) at the bottom.  At the top of step s the loads issued
+  // after A(s) include at least A(s+1), B(s) and B(s+1), so vmcnt <= APT + 2*NB means A(s)
+  // (and B(s)) have landed; the scale loads only make that count larger, so it stays safe.
   u32x4 b0[NT][BU], b1[NT][BU];
   float sc0[NT], zs0[NT], sc1[NT], zs1[NT];
-  load_a(0, ast);
+  issue_a(0, sA0);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(0, b0);
   load_scale(0, sc0, zs0);
-  store_a(0, ast);
-  load_a(1, ast);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(1, sA1);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(1, b1);
   load_scale(1, sc1, zs1);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int NB = NT * BU;                // weight loads per thread per step
+  constexpr int VM_A = APT + 2 * NB;
+  static_assert(VM_A < 64, "vmcnt field is 6 bits");
 
   // Dequantize word j of this step's weights into the 16-bit MFMA operand of each tile.
-  auto dequant = [&](int j, const float* sc, const float* zs, u32x4 (&Bq)[NT]) {
+  auto dequant = [&](const u32x4 (&bsrc)[NT][BU], int j, const float* sc, const float* zs, u32x4 (&Bq)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t w = b0[t][0][j];
+      const uint32_t w = bsrc[t][0][j];
       if constexpr (WP == WP_FP4) {
         Bq[t] = fp4_to_16<AF>(w, sc[t]);
       } else {
@@ -213,6 +228,39 @@ void mfma_gemm_kernel(MfmaArgs a) {
       }
     }
   };
+  // The same dequantization split into 4 stages per tile, so that it can be spread
+  // between MFMAs: stage 0 splits the nibbles, 1 and 2 convert and scale four elements
+  // each, 3 packs (e2m1: one hardware conversion per stage).
+  struct DQ {
+    uint32_t x0, x1;
+    float e[8];
+  };
+  auto dq_stage = [&](const u32x4 (&bsrc)[NT][BU], int j, int t, int stg, const float* sc, const float* zs,
+                      DQ& d, u32x4& out) {
+    const uint32_t w = bsrc[t][0][j];
+    if constexpr (WP == WP_FP4) {
+      out[stg] = (AF == A_F16) ? fp4_to_16<A_F16>(w, sc[t])[stg] : fp4_to_16<A_BF16>(w, sc[t])[stg];
+    } else {
+      if (stg == 0) {
+        d.x0 = w & 0x0F0F0F0Fu;
+        d.x1 = (w >> 4) & 0x0F0F0F0Fu;
+        asm volatile("" : "+v"(d.x0), "+v"(d.x1));   // keep v_cvt_f32_ubyteN (see dequant)
+      } else if (stg == 1) {
+        d.e[0] = __builtin_fmaf((float)(d.x0 & 0xFF), sc[t], zs[t]);
+        d.e[4] = __builtin_fmaf((float)((d.x0 >> 8) & 0xFF), sc[t], zs[t]);
+        d.e[1] = __builtin_fmaf((float)((d.x0 >> 16) & 0xFF), sc[t], zs[t]);
+        d.e[5] = __builtin_fmaf((float)(d.x0 >> 24), sc[t], zs[t]);
+      } else if (stg == 2) {
+        d.e[2] = __builtin_fmaf((float)(d.x1 & 0xFF), sc[t], zs[t]);
+        d.e[6] = __builtin_fmaf((float)((d.x1 >> 8) & 0xFF), sc[t], zs[t]);
+        d.e[3] = __builtin_fmaf((float)((d.x1 >> 16) & 0xFF), sc[t], zs[t]);
+        d.e[7] = __builtin_fmaf((float)(d.x1 >> 24), sc[t], zs[t]);
+      } else {
+        out = u32x4{pack2<AF>(d.e[0], d.e[1]), pack2<AF>(d.e[2], d.e[3]), pack2<AF>(d.e[4], d.e[5]),
+                    pack2<AF>(d.e[6], d.e[7])};
+      }
+    }
+  };
   // A fragments of 16-bit sub-step j (k = 32g + 8j of the step) for every row tile.
   auto read_a16 = [&](const uint8_t* sAb, int j, u32x4 (&Af)[MT]) {
 #pragma unroll
@@ -222,12 +270,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
     }
   };
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    __syncthreads();                                         // A(step) visible; other buffer free
-    store_a(buf ^ 1, ast);                                   // A(step+1) (zeros past the end)
-    load_a(step + 2, ast);                                   // out-of-range steps read nothing
-    const uint8_t* sAb = sA + buf * STAGE;
+  u32x4 Bq[2][NT];
+  if constexpr (!F8) dequant(b0, 0, sc0, zs0, Bq[0]);
+
+  // One K step; S = step % 3 is a compile-time stage index (the loop below is unrolled
+  // by three), so every LDS address names its stage array.
+  auto step_body = [&](const int step, auto S_) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    uint8_t* const sAb = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
+    uint8_t* const sAn = S == 0 ? sA2 : S == 1 ? sA0 : sA1;   // stage of step + 2
+    // this wave's A(step) loads have landed; the barrier makes every wave's visible and
+    // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_A & 15) | ((VM_A >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_a(step + 2, sAn);
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (F8) {
 #pragma unroll
@@ -251,21 +310,37 @@ void mfma_gemm_kernel(MfmaArgs a) {
         }
       }
     } else {
-      // Software pipeline over the 4 sub-steps: fragments and dequantized weights of
-      // sub-step j+1 are produced while the MFMAs of sub-step j run.
-      u32x4 Af[2][MT], Bq[2][NT];
+      // Software pipeline over the 4 sub-steps, ordered by hand: after the two MFMAs of
+      // each row tile come one stage of the next sub-step's dequantization and that tile's
+      // next activation fragment read; sched_barrier keeps the order.  Sub-step 3
+      // dequantizes sub-step 0 of the next step (its weights and scales are in registers).
+      u32x4 Af[2][MT];
       read_a16(sAb, 0, Af[0]);
-      dequant(0, sc0, zs0, Bq[0]);
+      constexpr int PH = NT * 4;                 // dequant stages per sub-step
+      constexpr int PPM = (PH + MT - 1) / MT;    // stages after each row tile
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j + 1 < 4) {
-          read_a16(sAb, j + 1, Af[(j + 1) & 1]);
-          dequant(j + 1, sc0, zs0, Bq[(j + 1) & 1]);
-        }
+        const bool last = (j == 3);
+        DQ dq[NT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[j & 1][mt], Bq[j & 1][t], acc[mt][t]);
+#pragma unroll
+          for (int q = 0; q < PPM; ++q) {
+            const int ph = mt * PPM + q;
+            if (ph < PH) {
+              const int t = ph / 4, stg = ph % 4;
+              if (last) dq_stage(b1, 0, t, stg, sc1, zs1, dq[t], Bq[(j + 1) & 1][t]);
+              else dq_stage(b0, j + 1, t, stg, sc0, zs0, dq[t], Bq[(j + 1) & 1][t]);
+            }
+          }
+          if (!last) {
+            const int row = 32 * (MT * wm + mt) + r;
+            Af[(j + 1) & 1][mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j + 1) ^ ((row >> 1) & 7)));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // rotate the weight and scale prefetch
@@ -276,9 +351,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
       sc0[t] = sc1[t];
       zs0[t] = zs1[t];
     }
+    __builtin_amdgcn_sched_barrier(0);
     load_b(step + 2, b1);
     load_scale(min(step + 2, nsteps - 1), sc1, zs1);
+  };
+  // The step count is padded to a multiple of three rather than leaving the unrolled
+  // loop early (early exits make the accumulators spill).  A padded step reads its
+  // activations out of range, i.e. zeros, so its MFMAs add exact zeros whatever the
+  // (finite) weights of that step dequantize to.
+  const int nsteps3 = (nsteps + 2) / 3 * 3;
+  for (int step = 0; step < nsteps3; step += 3) {
+    step_body(step, std::integral_constant<int, 0>{});
+    step_body(step + 1, std::integral_constant<int, 1>{});
+    step_body(step + 2, std::integral_constant<int, 2>{});
   }
+  // the two out-of-range A loads of the last steps are still writing (zeros) into LDS:
+  // let them land before the workgroup can finish and its LDS be handed to another
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: lane (r, g) of a 32x32 tile holds column r, rows 8*(i/4) + 4*g + i%4 ----
   uint16_t* yb = (uint16_t*)a.y;
@@ -308,8 +397,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // 256-row tiles run as 8 waves (2 row halves x 4 column quarters, 2 waves per SIMD)
-  constexpr int MW = BM == 256 ? 2 : 1;
-  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, MW>), grid, dim3(256 * MW), 0, st, a);
+  constexpr int MW = 1;
+  // two waves per SIMD: one workgroup of 8 waves (256 rows) or two workgroups of 4 (128 rows)
+  static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles");
+  constexpr int OCC = (WP == WP_FP8 || BM == 256) ? 1 : 2;   // 256x64 / fp8 wave tiles need > 256 registers
+  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, MW, OCC>), grid, dim3(256 * MW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
@@ -317,10 +409,12 @@ static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, 
   const dim3 grid(t.grid_x, t.grid_y);
   if (moe) {
     if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st); return true; }
-    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
+    if constexpr (WP != WP_FP8)
+      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
   } else {
     if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st); return true; }
-    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
+    if constexpr (WP != WP_FP8)
+      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
   }
   return false;
 }
