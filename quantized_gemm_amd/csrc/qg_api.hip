@@ -191,16 +191,43 @@ constexpr int64_t kStreamMaxRows = 64;
 // e4m3 weights and the int4 -> e4m3 path use 128-row tiles only.
 bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8 && pi.wp_mfma != WP_INT4Q_FP8; }
 
-MfmaTile mfma_tile(int64_t rows, int64_t n, const PathInfo& pi) {
+// Split K over workgroups when 128-row tiles would fill at most a quarter of the CUs
+// (above that, writing and re-reading the fp32 partials costs more than the idle CUs):
+// the largest power of two (at most 8) that keeps the grid within one workgroup per
+// CU, leaves every slice whole scale groups and at least 8 K steps.  Not for the
+// int4 -> e4m3 kernel.
+constexpr int kMaxSplit = 8;
+int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
+  if (pi.wp_mfma == WP_INT4Q_FP8 || tiles * 4 > kCUs) return 1;
+  const int64_t bk = pi.wp_mfma == WP_FP8 ? 128 : 64;
+  const int64_t steps = k / bk;
+  int sp = 1;
+  while (sp < kMaxSplit && tiles * sp * 2 <= kCUs && steps % (sp * 2) == 0 && steps / (sp * 2) >= 8 &&
+         (group <= 0 || (k / (sp * 2)) % group == 0))
+    sp *= 2;
+  return sp;
+}
+
+// Dense tiles (MoE tiles are built by qg_moe_gemm).
+MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo& pi) {
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
   t.bm = (mfma_rows256(pi) && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
   // experiment-only override of the row tile (QG_MFMA_BM=128|256)
   static const char* ov = getenv("QG_MFMA_BM");
   if (ov && mfma_rows256(pi) && (atoi(ov) == 128 || atoi(ov) == 256)) t.bm = atoi(ov);
-  t.grid_x = (unsigned)(((rows + t.bm - 1) / t.bm) * ntiles);
+  const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ntiles;
+  t.grid_x = (unsigned)tiles;
   t.grid_y = 1;
+  t.ksplit = t.bm == 128 ? split_for(tiles, k, group, pi) : 1;
   return t;
+}
+
+// Workspace of a dense call: the split-K partial sums.
+size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
+  if (m <= kStreamMaxRows) return 0;
+  const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
+  return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
 }
 
 }  // namespace
@@ -264,9 +291,10 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
 }
 
 size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk) {
-  (void)m_or_tokens; (void)topk;
-  (void)p;
-  return 0;   // no kernel of this version needs a workspace
+  PathInfo pi;
+  if (check_prepared(p, &pi) != QG_OK || m_or_tokens <= 0) return 0;
+  if (topk == 0 && p->desc.num_experts == 1) return dense_workspace(p, pi, m_or_tokens);
+  return 0;   // the grouped (MoE) kernels need none
 }
 
 static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
@@ -302,15 +330,24 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   if (m > (1 << 24) || !fits_rsrc(p, m)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
-  (void)ws; (void)ws_bytes;
   StreamArgs a{};
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
+  a.ksplit = 1;
   if (m > kStreamMaxRows) {
-    const MfmaTile t = mfma_tile(m, p->desc.n, pi);
-    QG_LOG("gemm m=%lld n=%lld k=%lld -> mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
-           (long long)p->desc.k, t.bm, t.grid_x);
+    const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
+    if (t.ksplit > 1) {
+      const size_t need = dense_workspace(p, pi, m);
+      if (!ws || !aligned16(ws) || ws_bytes < need) return QG_ERR_WORKSPACE;
+      a.part = (float*)ws;
+      a.ksplit = t.ksplit;
+    }
+    QG_LOG("gemm m=%lld n=%lld k=%lld -> mfma bm=%d grid=%u ksplit=%d", (long long)m, (long long)p->desc.n,
+           (long long)p->desc.k, t.bm, t.grid_x, t.ksplit);
     if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
+      return QG_ERR_UNSUPPORTED;
+    if (t.ksplit > 1 &&
+        !launch_split_reduce(a, pi.wp_mfma == WP_FP8, pi.af == A_FP8, pi.of, (hipStream_t)stream))
       return QG_ERR_UNSUPPORTED;
     return launched();
   }

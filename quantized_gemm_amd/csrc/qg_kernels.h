@@ -23,6 +23,8 @@ struct StreamArgs {
   const int32_t* expert_ids;
   const int32_t* num_post_pad;
   int topk, sentinel;
+  float* part;               // split K: fp32 partial sums [ksplit][m][n] (workspace)
+  int ksplit;                // K slices (1: none)
 };
 
 struct StreamTile {
@@ -36,9 +38,14 @@ typedef StreamArgs MfmaArgs;
 struct MfmaTile {
   int bm;                    // rows per workgroup tile (128 or 256); 256 columns per tile
   unsigned grid_x, grid_y;   // dense: grid_x = all tiles; MoE: grid_x = column tiles, grid_y = blocks
+  int ksplit;                // dense, 128-row tiles: K slices (grid z), 1 = none
 };
 bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int stype, bool zero, bool moe,
                       hipStream_t st);
+
+// Sum of the split-K partials a.part[ksplit][m][n] into a.y, with the e4m3 per-channel
+// (w_scale, fp8 weights) and per-token (a.x_scale, e4m3 activations) scales.
+bool launch_split_reduce(const MfmaArgs& a, bool w_scale, bool x_scale, int of, hipStream_t st);
 
 bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af, int of, int stype, bool zero,
                         bool moe, hipStream_t st);

@@ -26,7 +26,7 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, int MW, int OCC>
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int MW, int OCC>
 __global__ __launch_bounds__(256 * MW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (WP == WP_FP8);
@@ -98,7 +98,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
   const int nb_count = a.n >> 4;
   const int64_t col0 = (int64_t)ntile * BN + 64 * wave;     // first column of this wave
-  const int nsteps = a.k / BK;
+  // Split K: workgroup z owns steps [kstep0, kstep0 + nsteps) and writes fp32 partial
+  // sums (the host makes the slices whole scale groups); otherwise all of K.
+  const int nsteps = SPLIT ? a.k / BK / a.ksplit : a.k / BK;
+  const int kstep0 = SPLIT ? (int)blockIdx.z * nsteps : 0;
   const int64_t kun = F8 ? (a.k >> 4) : (a.k >> 5);
   const int ngroups = a.group == 0 ? 1 : a.k / a.group;
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
@@ -124,7 +127,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
   auto issue_a = [&](int step, uint8_t* stage) {
 #pragma unroll
     for (int i = 0; i < APT; ++i)
-      bload16_lds(xr, stage + NTHR * 16 * i + wave_slot, a_off[i] < 0 || step >= nsteps ? kOOB : a_off[i] + step * ROWB);
+      bload16_lds(xr, stage + NTHR * 16 * i + wave_slot,
+                  a_off[i] < 0 || step >= nsteps ? kOOB : a_off[i] + (kstep0 + step) * ROWB);
   };
 
   // ---- weights: per tile t, this lane's column and 16-byte units for a step ----------
@@ -142,7 +146,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int u = 0; u < BU; ++u) {
         // 4-bit: unit (step*2 + g) covers k = 64*step + 32g ..; fp8: units 8*step + 4g + u
-        const int64_t ku = F8 ? ((int64_t)step * 8 + 4 * g + u) : ((int64_t)step * 2 + g);
+        const int64_t gs = (int64_t)(kstep0 + step);
+        const int64_t ku = F8 ? (gs * 8 + 4 * g + u) : (gs * 2 + g);
         const bool ok = wok[t] && step < nsteps;
         dst[t][u] = bload16_stream(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
       }
@@ -154,11 +159,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
     for (int t = 0; t < NT; ++t) {
       const int64_t nb = min((int64_t)nb_count - 1, wcol[t] >> 4), c = wcol[t] & 15;
       if constexpr (WP == WP_FP4) {
-        const int64_t gi = (int64_t)step * 2 + g;           // group 32 == unit
+        const int64_t gi = (int64_t)(kstep0 + step) * 2 + g;   // group 32 == unit
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         zs[t] = 0.f;
       } else if constexpr (WP == WP_INT4_MAGIC) {
-        const int gi = a.group == 0 ? 0 : (step * BK) / a.group;
+        const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         float z = 8.0f;
         if constexpr (ZERO) {
@@ -182,22 +187,33 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][t][i] = 0.f;
 
-  // ---- prologue: A(0), A(1) -> LDS stages 0, 1; weights and scales of steps 0 and 1 --
-  // Vector-memory issue order, kept by sched_barrier: A(0) B(0) A(1) B(1), then per step s
-  // A(s+2) at the top and B(s+2) at the bottom.  At the top of step s the loads issued
-  // after A(s) include at least A(s+1), B(s) and B(s+1), so vmcnt <= APT + 2*NB means A(s)
-  // (and B(s)) have landed; the scale loads only make that count larger, so it stays safe.
-  u32x4 b0[NT][BU], b1[NT][BU];
-  float sc0[NT], zs0[NT], sc1[NT], zs1[NT];
+  // ---- prologue: A(0), A(1) -> LDS stages 0, 1; weights and scales -------------------
+  // Weights and scales live in a ring of three register sets, slot = step % 3 (a
+  // compile-time index in the unrolled loop), loaded DIST steps ahead.  16-bit
+  // activations: DIST = 3, since the last sub-step of step s already dequantizes step
+  // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
+  // idle and its registers free for other values.  Vector-memory issue order, kept by
+  // sched_barrier: [B(0)] A(0) B(DIST-2) A(1) B(DIST-1), then per step s A(s+2) at the top
+  // and B(s+DIST) at the bottom.  At the top of step s the loads issued after A(s)
+  // include at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <= APT + 2*NB means
+  // A(s) has landed; the scale loads only make that count larger, so the wait is safe.
+  constexpr int DIST = F8 ? 2 : 3;
+  u32x4 bw[3][NT][BU];
+  float scl[3][NT], zsl[3][NT];
+  if constexpr (DIST == 3) {
+    load_b(0, bw[0]);
+    load_scale(0, scl[0], zsl[0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   issue_a(0, sA0);
   __builtin_amdgcn_sched_barrier(0);
-  load_b(0, b0);
-  load_scale(0, sc0, zs0);
+  load_b(DIST - 2, bw[DIST - 2]);
+  load_scale(min(DIST - 2, nsteps - 1), scl[DIST - 2], zsl[DIST - 2]);
   __builtin_amdgcn_sched_barrier(0);
   issue_a(1, sA1);
   __builtin_amdgcn_sched_barrier(0);
-  load_b(1, b1);
-  load_scale(1, sc1, zs1);
+  load_b(DIST - 1, bw[DIST - 1]);
+  load_scale(min(DIST - 1, nsteps - 1), scl[DIST - 1], zsl[DIST - 1]);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int NB = NT * BU;                // weight loads per thread per step
   constexpr int VM_A = APT + 2 * NB;
@@ -271,7 +287,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   };
 
   u32x4 Bq[2][NT];
-  if constexpr (!F8) dequant(b0, 0, sc0, zs0, Bq[0]);
+  if constexpr (!F8) dequant(bw[0], 0, scl[0], zsl[0], Bq[0]);
 
   // One K step; S = step % 3 is a compile-time stage index (the loop below is unrolled
   // by three), so every LDS address names its stage array.
@@ -287,6 +303,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
     asm volatile("" ::: "memory");
     issue_a(step + 2, sAn);
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
+    auto& b0 = bw[S];
+    auto& b1 = bw[S1];
+    // Pin the next step's scales as plain register values here, where their loads are
+    // two steps old (left as "-8 * s" the symmetric form sends the register allocator
+    // into heavy spilling; pinned at the load, it would wait for the load at once).
+#pragma unroll
+    for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(scl[S1][t]), "+v"(zsl[S1][t]));
 
     if constexpr (F8) {
 #pragma unroll
@@ -331,8 +355,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
             const int ph = mt * PPM + q;
             if (ph < PH) {
               const int t = ph / 4, stg = ph % 4;
-              if (last) dq_stage(b1, 0, t, stg, sc1, zs1, dq[t], Bq[(j + 1) & 1][t]);
-              else dq_stage(b0, j + 1, t, stg, sc0, zs0, dq[t], Bq[(j + 1) & 1][t]);
+              if (last) dq_stage(b1, 0, t, stg, scl[S1], zsl[S1], dq[t], Bq[(j + 1) & 1][t]);
+              else dq_stage(b0, j + 1, t, stg, scl[S], zsl[S], dq[t], Bq[(j + 1) & 1][t]);
             }
           }
           if (!last) {
@@ -343,17 +367,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
         }
       }
     }
-    // rotate the weight and scale prefetch
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int u = 0; u < BU; ++u) b0[t][u] = b1[t][u];
-      sc0[t] = sc1[t];
-      zs0[t] = zs1[t];
-    }
+    // weights and scales of step + DIST into their slot (DIST = 3: this step's, now free)
+    constexpr int SL = (S + DIST) % 3;
     __builtin_amdgcn_sched_barrier(0);
-    load_b(step + 2, b1);
-    load_scale(min(step + 2, nsteps - 1), sc1, zs1);
+    load_b(step + DIST, bw[SL]);
+    load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
   };
   // The step count is padded to a multiple of three rather than leaving the unrolled
   // loop early (early exits make the accumulators spill).  A padded step reads its
@@ -370,6 +388,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: lane (r, g) of a 32x32 tile holds column r, rows 8*(i/4) + 4*g + i%4 ----
+  if constexpr (SPLIT) {
+    // raw fp32 partial sums of this K slice; the reduction applies the scales
+    float* pb = a.part + (int64_t)blockIdx.z * a.m * a.n;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!wok[t]) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * (MT * wm + mt) + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (sRowTok[row] < 0) continue;
+          pb[(rowbase + row) * a.n + wcol[t]] = acc[mt][t][i];
+        }
+    }
+    return;
+  }
   uint16_t* yb = (uint16_t*)a.y;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -394,14 +429,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
   }
 }
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE>
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT = false>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // 256-row tiles run as 8 waves (2 row halves x 4 column quarters, 2 waves per SIMD)
   constexpr int MW = 1;
   // two waves per SIMD: one workgroup of 8 waves (256 rows) or two workgroups of 4 (128 rows)
   static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles");
   constexpr int OCC = (WP == WP_FP8 || BM == 256) ? 1 : 2;   // 256x64 / fp8 wave tiles need > 256 registers
-  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, MW, OCC>), grid, dim3(256 * MW), 0, st, a);
+  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, MW, OCC>), grid, dim3(256 * MW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
@@ -412,6 +447,11 @@ static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, 
     if constexpr (WP != WP_FP8)
       if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
   } else {
+    if (t.ksplit > 1) {
+      if (t.bm != 128) return false;
+      launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false, true>(a, dim3(t.grid_x, t.grid_y, t.ksplit), st);
+      return true;
+    }
     if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st); return true; }
     if constexpr (WP != WP_FP8)
       if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }

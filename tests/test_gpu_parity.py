@@ -255,3 +255,40 @@ def test_moe_w4a8_int4_mfma_path(t):
     layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=13)
     y = _run_moe(layer, acts)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
+
+
+# ---- split K (few output tiles: K is split over workgroups, partials summed in order) ----
+
+@pytest.mark.parametrize("m,k", [(65, 4096), (128, 8192), (200, 2048)])
+def test_dense_split_k(m, k):
+    # 2 / 2 / 4 output tiles of 128 x 256: K split 8 / 8 / 4 ways
+    layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=512, k=k, seed=14)
+    p, _ = layers.prepare_layer(layer)
+    assert qg.workspace_bytes(p, m) > 0
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+def test_dense_w8a8_fp8_split_k():
+    layer, acts = synth.dense_w8a8_fp8(m=100, n=256, k=4096, seed=15)
+    y = _run_dense(layer, acts, 100)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
+
+
+def test_dense_split_k_is_deterministic_and_checks_workspace():
+    layer, acts = synth.dense_w4a16_asym_bf16(m=96, n=256, k=2048, seed=16)
+    p, buf = layers.prepare_layer(layer)
+    x, _ = layers.acts_to_dev(acts)
+    need = qg.workspace_bytes(p, 96)
+    assert need == 4 * 96 * 256 * 4      # 32 K steps: 4 slices of 8
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y1 = torch.empty((96, 256), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    qg.gemm(p, x, None, y1, 96, ws)
+    qg.gemm(p, x, None, y2, 96, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(qg.QGError):
+        qg.gemm(p, x, None, y1, 96, ws[: need - 16])
+    with pytest.raises(qg.QGError):
+        qg.gemm(p, x, None, y1, 96, None)
