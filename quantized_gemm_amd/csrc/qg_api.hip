@@ -191,14 +191,14 @@ constexpr int64_t kStreamMaxRows = 64;
 // e4m3 weights and the int4 -> e4m3 path use 128-row tiles only.
 bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8 && pi.wp_mfma != WP_INT4Q_FP8; }
 
-// Split K over workgroups when 128-row tiles would fill at most a quarter of the CUs
-// (above that, writing and re-reading the fp32 partials costs more than the idle CUs):
+// Split K over workgroups when 128-row tiles would fill at most half of the CUs (above
+// that, writing and re-reading the fp32 partials costs more than the idle CUs):
 // the largest power of two (at most 8) that keeps the grid within one workgroup per
 // CU, leaves every slice whole scale groups and at least 8 K steps.  Not for the
 // int4 -> e4m3 kernel.
 constexpr int kMaxSplit = 8;
 int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
-  if (pi.wp_mfma == WP_INT4Q_FP8 || tiles * 4 > kCUs) return 1;
+  if (pi.wp_mfma == WP_INT4Q_FP8 || tiles * 2 > kCUs) return 1;
   const int64_t bk = pi.wp_mfma == WP_FP8 ? 128 : 64;
   const int64_t steps = k / bk;
   int sp = 1;
@@ -220,6 +220,14 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   t.grid_x = (unsigned)tiles;
   t.grid_y = 1;
   t.ksplit = t.bm == 128 ? split_for(tiles, k, group, pi) : 1;
+  // experiment-only override of the split (QG_KSPLIT=1|2|4|8; slices must stay whole groups)
+  static const char* ks = getenv("QG_KSPLIT");
+  if (ks && t.bm == 128 && pi.wp_mfma != WP_INT4Q_FP8) {
+    const int v = atoi(ks);
+    const int64_t bk = pi.wp_mfma == WP_FP8 ? 128 : 64;
+    if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / bk) % v == 0 && (group <= 0 || (k / v) % group == 0))
+      t.ksplit = v;
+  }
   return t;
 }
 

@@ -48,6 +48,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sA1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sA2[STAGE];
   __shared__ int sRowTok[BM];
+  __shared__ int sRowOut[BM];    // output row of each tile row (-1: none)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,13 +87,17 @@ void mfma_gemm_kernel(MfmaArgs a) {
   for (int i = tid; i < BM; i += NTHR) {
     const int64_t rr = rowbase + i;
     int tok;
+    int orow;
     if constexpr (MOE) {
       const int f = a.sorted_ids[rr];
       tok = f < a.sentinel ? f / a.topk : -1;
+      orow = f;
     } else {
       tok = rr < a.m ? (int)rr : -1;
+      orow = (int)rr;
     }
     sRowTok[i] = tok;
+    sRowOut[i] = tok < 0 ? -1 : orow;
   }
   __syncthreads();
 
@@ -387,45 +392,65 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // let them land before the workgroup can finish and its LDS be handed to another
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // ---- epilogue: lane (r, g) of a 32x32 tile holds column r, rows 8*(i/4) + 4*g + i%4 ----
-  if constexpr (SPLIT) {
-    // raw fp32 partial sums of this K slice; the reduction applies the scales
-    float* pb = a.part + (int64_t)blockIdx.z * a.m * a.n;
+  // ---- epilogue ----------------------------------------------------------------------
+  // Lane (r, g) of a 32x32 tile holds column r, rows 8*(i/4) + 4*g + i%4.  Each wave
+  // stages CR rows x its 64 columns in LDS (the activation stages are free now), then
+  // writes whole row segments with 16-byte stores: 128 bytes per output row (16-bit)
+  // or 256 bytes (fp32 split-K partials, unscaled: the reduction applies the scales).
+  __syncthreads();                                   // every wave is done with the stages
+  if (!wok[0]) return;                               // n % 64 == 0: all or none of the 64 columns
+  constexpr int OB = SPLIT ? 4 : 2;                  // output bytes per element
+  constexpr int CR = SPLIT ? 16 : 32;                // rows per staged chunk
+  constexpr int PITCH = 64 * OB + 16;                // padded LDS row
+  static_assert(2 * CR * PITCH <= STAGE, "two waves' chunks per stage array");
+  uint8_t* const ep = (wave < 2 ? sA0 : sA1) + (wave & 1) * CR * PITCH;
+  const int64_t col0w = col0;                        // first column of this wave
+  float sw[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (!wok[t]) continue;
+  for (int t = 0; t < NT; ++t) sw[t] = F8 && !SPLIT ? ((const float*)a.s)[(int64_t)expert * a.n + wcol[t]] : 1.f;
+  constexpr int HALVES = 32 / CR;                    // chunks per 32-row tile
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+      const int rbase = 32 * (MT * wm + mt) + CR * h;          // first tile row of the chunk
+      // stage: element (row, col) of the chunk at ep + row * PITCH + col * OB
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = 32 * (MT * wm + mt) + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (sRowTok[row] < 0) continue;
-          pb[(rowbase + row) * a.n + wcol[t]] = acc[mt][t][i];
+          if ((8 * (i >> 2)) / CR != h) continue;              // rows of element i: 8(i/4) + 0..7
+          const int rl = 8 * (i >> 2) + 4 * g + (i & 3) - CR * h;
+          float v = acc[mt][t][i];
+          if constexpr (SPLIT) {
+            *(float*)(ep + rl * PITCH + (32 * t + r) * 4) = v;
+          } else {
+            v *= sw[t];
+            if constexpr (AF == A_FP8) {
+              const int tok = sRowTok[rbase + rl];
+              v *= tok < 0 ? 0.f : a.x_scale[tok];
+            }
+            *(uint16_t*)(ep + rl * PITCH + (32 * t + r) * 2) = f32_to_out<OF>(v);
+          }
         }
-    }
-    return;
-  }
-  uint16_t* yb = (uint16_t*)a.y;
+      // write: CR rows x 64 * OB bytes = CR * 4 * OB pieces of 16 bytes, 64 per lane pass
+      constexpr int PPR = 64 * OB / 16;                        // pieces per row
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int64_t n = wcol[t];
-    if (!wok[t]) continue;
-    float sw = 1.f;
-    if constexpr (F8) sw = ((const float*)a.s)[(int64_t)expert * a.n + n];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * (MT * wm + mt) + 8 * (i >> 2) + 4 * g + (i & 3);
-        const int tok = sRowTok[row];
-        if (tok < 0) continue;
-        float v = acc[mt][t][i] * sw;
-        if constexpr (AF == A_FP8) v *= a.x_scale[tok];
-        int64_t orow;
-        if constexpr (MOE) orow = a.sorted_ids[rowbase + row];
-        else orow = rowbase + row;
-        yb[orow * a.n + n] = f32_to_out<OF>(v);
+      for (int q = 0; q < CR * PPR / 64; ++q) {
+        const int pc = lane + 64 * q;
+        const int rl = pc / PPR, c16 = pc - rl * PPR;
+        const int orow = sRowOut[rbase + rl];
+        if (orow < 0) continue;
+        const u32x4 val = *(const u32x4*)(ep + rl * PITCH + 16 * c16);
+        if constexpr (SPLIT) {
+          float* dst = a.part + ((int64_t)blockIdx.z * a.m + orow) * a.n + col0w + 4 * c16;
+          *(u32x4*)dst = val;
+        } else {
+          uint16_t* dst = (uint16_t*)a.y + (int64_t)orow * a.n + col0w + 8 * c16;
+          *(u32x4*)dst = val;
+        }
       }
+    }
   }
 }
 
