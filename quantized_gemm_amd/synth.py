@@ -71,15 +71,27 @@ def absmax_e4m3_rows(x: np.ndarray):
 
 
 def pack_nibbles_u32(nib: np.ndarray) -> np.ndarray:
-    """[.., K] values 0..15 -> uint32 [.., K/8], element k at bits 4*(k%8) (low nibble first)."""
-    nib = np.asarray(nib, dtype=np.uint32)
+    """[.., K] values 0..15 -> uint32 [.., K/8], element k at bits 4*(k%8) (low nibble first).
+
+    Packs byte pairs (even k low) and reads four bytes as one little-endian word, which
+    puts element k at bits 4*(k%8); no wider-than-byte temporaries (full-size MoE layers
+    hold billions of codes)."""
+    nib = np.asarray(nib)
     *lead, k = nib.shape
     assert k % 8 == 0
-    v = nib.reshape(*lead, k // 8, 8)
-    out = np.zeros((*lead, k // 8), dtype=np.uint32)
-    for i in range(8):
-        out |= v[..., i] << np.uint32(4 * i)
-    return out
+    b = np.ascontiguousarray(pack_nibbles_u8(nib.astype(np.uint8, copy=False)))
+    return b.view("<u4").reshape(*lead, k // 8)
+
+
+def random_nibbles_u32(rng: np.random.Generator, lead: tuple, k: int) -> np.ndarray:
+    """Uniform 4-bit codes, packed like pack_nibbles_u32: [*lead, K/8] uint32.
+
+    A uniform random byte is two independent uniform nibbles (element 2j low, 2j+1 high),
+    so the bytes are drawn directly; read as two's complement a nibble is uniform over
+    [-8, 7], as an unsigned code uniform over [0, 15]."""
+    assert k % 8 == 0
+    b = rng.integers(0, 256, size=(*lead, k // 2), dtype=np.uint8)
+    return b.view("<u4").reshape(*lead, k // 8)
 
 
 def pack_nibbles_u8(nib: np.ndarray) -> np.ndarray:
@@ -134,9 +146,8 @@ def dense_w4a16_sym_f16(m: int = 16, n: int = 512, k: int = 1024, group: int = 1
     """Dense W4A16, symmetric int4 in [-8, 7], fp16 group scales in [0.005, 0.02], fp16 activations."""
     rng = _rng(seed)
     x = f32_to_f16_bits(rng.standard_normal((m, k), dtype=np.float32))
-    q = rng.integers(-8, 8, size=(1, n, k), dtype=np.int64)
+    w = random_nibbles_u32(rng, (1, n), k)          # two's complement codes: q uniform in [-8, 7]
     s = f32_to_f16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
-    w = pack_nibbles_u32((q & 0xF).astype(np.uint32))
     layer = Layer("dense_w4a16_sym_f16", "int4", "f16", "f16", "f16", n, k, group, 1, w, s, None)
     return layer, Acts(x, None, None)
 
@@ -145,10 +156,9 @@ def dense_w4a16_asym_bf16(m: int = 16, n: int = 8192, k: int = 8192, group: int 
     """Dense W4A16, uint4 codes in [0, 15] with uint4 zero points in [6, 9], bf16 group scales."""
     rng = _rng(seed)
     x = f32_to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
-    u = rng.integers(0, 16, size=(1, n, k), dtype=np.int64)
+    w = random_nibbles_u32(rng, (1, n), k)          # u uniform in [0, 15]
     s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
-    z = rng.integers(6, 10, size=(1, n, k // group), dtype=np.int64).astype(np.uint8)
-    w = pack_nibbles_u32(u.astype(np.uint32))
+    z = rng.integers(6, 10, size=(1, n, k // group), dtype=np.uint8)
     layer = Layer("dense_w4a16_asym_bf16", "uint4", "bf16", "bf16", "bf16", n, k, group, 1, w, s, z)
     return layer, Acts(x, None, None)
 
@@ -186,7 +196,7 @@ def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, 
     +3.0 on the logits of four hot experts before top-k."""
     rng = _rng(seed)
     xq, sx = absmax_e4m3_rows(rng.standard_normal((t, k), dtype=np.float32))
-    q = rng.integers(-8, 8, size=(experts, n, k), dtype=np.int64)
+    w = random_nibbles_u32(rng, (experts, n), k)    # two's complement codes: q uniform in [-8, 7]
     s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(experts, n, k // group)).astype(np.float32))
     logits = rng.standard_normal((t, experts), dtype=np.float32)
     n_hot = int(round(hot_frac * t))
@@ -195,7 +205,6 @@ def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, 
         if e < experts:
             logits[hot_tokens, e] += np.float32(hot_bias)
     ids = topk_from_logits(logits, topk)
-    w = pack_nibbles_u32((q & 0xF).astype(np.uint32))
     layer = Layer("moe_w4a8_int4", "int4", "e4m3", "bf16", "bf16", n, k, group, experts, w, s, None,
                   compute="w_to_fp8")
     return layer, Acts(xq, sx, ids)
