@@ -4,6 +4,7 @@
 // M get their own configurations, chosen by where computation starts to dominate
 // weight transfer) and the launch is enqueued on the caller's stream.
 #include <stdio.h>
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -370,12 +371,20 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
 int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   PathInfo pi;
   if (check_prepared(p, &pi) != QG_OK || tokens < 0 || topk <= 0) return 0;
-  const int64_t rows = tokens * topk;
-  const int64_t per_expert = (rows + p->desc.num_experts - 1) / p->desc.num_experts;
-  if (per_expert <= 16) return 16;
-  if (per_expert <= 32) return 32;
-  if (per_expert <= 96) return 64;
-  if (per_expert < 512 || !mfma_rows256(pi)) return 128;
+  // With a mean of m rows per expert, counts spread about sqrt(m) (multinomial routing).
+  // The streaming family is kept while the busier experts, mean + 3 sqrt(mean) rows, fit
+  // in its largest block (64 rows): beyond that most experts would stream their weights
+  // two or more times, and 128-row MFMA blocks win.  Within the streaming family the
+  // block follows the mean (a bigger block re-stages more activation rows per round,
+  // which costs more than the occasional second pass over an expert's weights).
+  const double rows = (double)tokens * topk;
+  const double mean = rows / p->desc.num_experts;
+  if (mean + 3.0 * sqrt(mean) <= 64) {
+    if (mean <= 16) return 16;
+    if (mean <= 32) return 32;
+    return 64;
+  }
+  if (mean < 512 || !mfma_rows256(pi)) return 128;
   return 256;
 }
 
