@@ -67,18 +67,30 @@ void mfma_gemm_kernel(MfmaArgs a) {
     if (rowbase >= (int64_t)(*a.num_post_pad)) return;
     expert = a.expert_ids[blockIdx.y];
   } else {
-    // The dispatcher hands workgroups to the 8 XCDs round-robin (XCD = id % 8).  When
-    // the column tiles split evenly, XCD x owns a contiguous band of column tiles and
-    // walks its row tiles row-major over that band, so the ~32 tiles it runs at once
-    // share a few activation row blocks and weight column blocks in its own L2.
+    // The dispatcher hands workgroups to the 8 XCDs round-robin (XCD = id % 8), each XCD
+    // with its own L2.  The tile grid is cut into XR x (8 / XR) blocks, one per XCD, with
+    // XR chosen so that an XCD's share of activation rows plus weight columns is
+    // smallest (each XCD then fetches only its own rows and columns); inside its block
+    // an XCD walks row tiles fastest, so the ~32 tiles it runs at once form a compact
+    // rectangle sharing activation and weight slices in L2.
     const int mtiles = (int)((a.m + BM - 1) / BM);
     const int ntiles = (int)gridDim.x / mtiles;
     const int id = blockIdx.x;
-    if ((ntiles & 7) == 0) {
-      const int nper = ntiles >> 3;
-      const int x = id & 7, l = id >> 3;
-      ntile = x * nper + l % nper;
-      rowbase = (int64_t)(l / nper) * BM;
+    const int64_t rowb = (int64_t)a.k * AB, colb = F8 ? a.k : a.k / 2;   // bytes per row / column
+    int xr = 0;
+    int64_t best = 0;
+    for (int cand = 1; cand <= 8; cand <<= 1) {
+      if (mtiles % cand != 0 || ntiles % (8 / cand) != 0) continue;
+      const int64_t cost = (int64_t)mtiles * BM * rowb / cand + (int64_t)ntiles * BN * colb / (8 / cand);
+      if (xr == 0 || cost < best) { xr = cand; best = cost; }
+    }
+    if (xr != 0) {
+      const int xc = 8 / xr;
+      const int mt_x = mtiles / xr, nt_x = ntiles / xc;   // tiles per XCD block
+      const int x = id & 7, l = id >> 3;                   // XCD and its local tile index
+      const int lm = l % mt_x, ln = l / mt_x;
+      rowbase = (int64_t)((x / xc) * mt_x + lm) * BM;
+      ntile = (x % xc) * nt_x + ln;
     } else {
       ntile = id / mtiles;
       rowbase = (int64_t)(id - ntile * mtiles) * BM;
