@@ -184,6 +184,9 @@ qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, in
  * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
  *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3, else NULL
  *   sorted_ids / expert_ids / num_post_pad  from qg_moe_align with the same block_m
+ *   block_m  4, 16, 32 or 64 (weight-streaming kernel) or 128, 256 (MFMA kernel; 256 not
+ *            for e4m3 or int4->e4m3 weights); qg_moe_block_m picks one, any other is
+ *            QG_ERR_UNSUPPORTED
  *   y        device [T*topk][N] of out_type; rows of dropped slots are not written
  * The grid is sized from capacity; blocks past num_post_pad exit at once.
  */

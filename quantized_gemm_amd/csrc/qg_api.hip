@@ -172,15 +172,16 @@ qg_status launched() {
 
 // ---- M-bucket selector --------------------------------------------------------------
 // Weight-streaming family: a workgroup of 2 column blocks x 4 K parts (4-bit weights)
-// or 1 x 8 (e4m3 weights) waves; rows in blocks of 16 / 32 / 64.
+// or 1 x 8 (e4m3 weights) waves; rows in blocks of 4 / 16 / 32 / 64 (mt = 0 / 1 / 2 / 4).
 StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
   StreamTile t{};
   const bool w8 = w_type == QG_W_FP8_E4M3;
   t.ncb = w8 ? 1 : 2;
   t.kq = w8 ? 8 : 4;
-  t.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  t.mt = rows <= 4 ? 0 : (rows <= 16 ? 1 : (rows <= 32 ? 2 : 4));
+  const int64_t bm = t.mt == 0 ? 4 : 16 * t.mt;
   t.grid_x = (unsigned)((n / 16 + t.ncb - 1) / t.ncb);
-  t.grid_y = (unsigned)((rows + 16 * t.mt - 1) / (16 * t.mt));
+  t.grid_y = (unsigned)((rows + bm - 1) / bm);
   return t;
 }
 
@@ -379,6 +380,7 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   // which costs more than the occasional second pass over an expert's weights).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
+  if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
     if (mean <= 16) return 16;
     if (mean <= 32) return 32;
@@ -429,7 +431,8 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   if (!x || !y || !sorted_ids || !expert_ids || !num_post_pad || !aligned16(x) || !aligned16(y))
     return QG_ERR_INVALID_ARG;
   if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
-  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return QG_ERR_UNSUPPORTED;
+  if (block_m != 4 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256)
+    return QG_ERR_UNSUPPORTED;
   if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();

@@ -23,7 +23,7 @@
 // are staged in LDS in rounds (the next round's staging loads are in flight while the
 // current round computes); the KQ partial sums of a column block are added through LDS
 // in a fixed order at the end.  No workspace, no atomics, deterministic.
-// Grid: x = groups of NCB column blocks, y = row blocks of 16*MT rows (dense) or MoE
+// Grid: x = groups of NCB column blocks, y = row blocks of 16*MT (MT = 0: 4) rows (dense) or MoE
 // blocks (rows gathered through sorted_ids).
 #pragma once
 
@@ -48,9 +48,10 @@ constexpr int stream_max_chunks() { return WP == WP_FP8 ? 8 : 16; }
 // Chunks per K part staged per round: <= 64 KB of activations in LDS.
 template <int WP, int AF, int MT, int KQ>
 constexpr int stream_round_chunks() {
-  constexpr int per_chunk = 16 * MT * KQ * 128 * StreamTraits<WP, AF>::ABYTES;
+  constexpr int per_chunk = (MT == 0 ? 4 : 16 * MT) * KQ * 128 * StreamTraits<WP, AF>::ABYTES;
   constexpr int rc = (64 * 1024) / per_chunk;
-  return rc < 1 ? 1 : (rc > 16 ? 16 : rc);
+  constexpr int cap = stream_max_chunks<WP>();       // a round never spans two weight batches
+  return rc < 1 ? 1 : (rc > cap ? cap : rc);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NCB, int KQ, bool MOE>
@@ -58,9 +59,13 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   using T = StreamTraits<WP, AF>;
   constexpr int NW = NCB * KQ;
   constexpr int NTHR = 64 * NW;
-  constexpr int BM = 16 * MT;
+  // MT 16-row MFMA tiles; MT == 0 is a 4-row tile (one MFMA tile whose rows 4..15 are
+  // zero operands, never staged): for 1..4 rows, the whole K of every part fits one round.
+  constexpr int BM = MT == 0 ? 4 : 16 * MT;
+  constexpr int NMT = MT == 0 ? 1 : MT;
   constexpr int RCR = stream_round_chunks<WP, AF, MT, KQ>();   // chunks per part per round
   constexpr int CHMAX = stream_max_chunks<WP>();
+  static_assert(CHMAX % RCR == 0, "whole rounds per weight batch");
   constexpr int PART = RCR * 128 * T::ABYTES;                   // bytes of one part's round in an LDS row
   constexpr int AROW = KQ * PART + 16;                          // padded LDS row (bytes)
   constexpr int SB = T::SBYTES > 0 ? T::SBYTES : 16;
@@ -191,9 +196,13 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     }
   };
 
-  f32x4 acc[MT];
+  f32x4 acc[NMT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the lane's activation row within a 16-row tile: staged rows only (4-row tiles: rows
+  // 4..15 read row r & 3 and are then zeroed)
+  const int ar = MT == 0 ? (r & 3) : r;
+  const bool aok = MT != 0 || r < 4;
 
   const int nrounds = (per + RCR - 1) / RCR;
 
@@ -232,13 +241,13 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
             const int slot = (cb * KQ + q) * RCR + lc;
             if constexpr (WP == WP_FP8) {
     #pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* ap = arow0 + (16 * mt + r) * AROW + 32 * g;
+              for (int mt = 0; mt < NMT; ++mt) {
+                const uint8_t* ap = arow0 + (16 * mt + ar) * AROW + 32 * g;
                 const u32x4 a0 = *(const u32x4*)ap, a1 = *(const u32x4*)(ap + 16);
                 i32x8 A, B;
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  A[i] = (int)a0[i]; A[4 + i] = (int)a1[i];
+                  A[i] = aok ? (int)a0[i] : 0; A[4 + i] = aok ? (int)a1[i] : 0;
                   B[i] = (int)bw[c][0][i]; B[4 + i] = (int)bw[c][1][i];
                 }
                 acc[mt] = mfma16x16x128_fp8(A, B, acc[mt]);
@@ -252,8 +261,9 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
               for (int j = 0; j < 4; ++j) {
                 const u32x4 b = fp4_to_16<AF>(bw[c][0][j], sc);
     #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                  const u32x4 av = *(const u32x4*)(arow0 + (16 * mt + r) * AROW + (32 * g + 8 * j) * 2);
+                for (int mt = 0; mt < NMT; ++mt) {
+                  u32x4 av = *(const u32x4*)(arow0 + (16 * mt + ar) * AROW + (32 * g + 8 * j) * 2);
+                  if (!aok) av = u32x4{0u, 0u, 0u, 0u};
                   acc[mt] = mfma16x16x32<AF>(av, b, acc[mt]);
                 }
               }
@@ -263,9 +273,9 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
               constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
               constexpr uint32_t ONE2 = (MAF == A_F16) ? 0x3C003C00u : 0x3F803F80u;
               const u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
-              f32x4 P[MT], R[MT];
+              f32x4 P[NMT], R[NMT];
     #pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
+              for (int mt = 0; mt < NMT; ++mt) {
                 P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 R[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
               }
@@ -275,15 +285,16 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                 if constexpr (QUAD) wj ^= 0x88888888u;      // two's complement -> q + 8
                 const u32x4 b = magic4<MAF>(wj);
     #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int mt = 0; mt < NMT; ++mt) {
                   u32x4 av;
                   if constexpr (AF == A_FP8) {
-                    const u32x2 e = *(const u32x2*)(arow0 + (16 * mt + r) * AROW + 32 * g + 8 * j);
+                    const u32x2 e = *(const u32x2*)(arow0 + (16 * mt + ar) * AROW + 32 * g + 8 * j);
                     av = e4m3x8_to_bf16_quad(e[0], e[1]);
                   } else {
-                    av = *(const u32x4*)(arow0 + (16 * mt + r) * AROW + (32 * g + 8 * j) * 2);
+                    av = *(const u32x4*)(arow0 + (16 * mt + ar) * AROW + (32 * g + 8 * j) * 2);
                     if constexpr (QUAD) av = a16_to_quad(av);
                   }
+                  if (!aok) av = u32x4{0u, 0u, 0u, 0u};
                   R[mt] = mfma16x16x32<MAF>(av, ones, R[mt]);
                   P[mt] = mfma16x16x32<MAF>(av, b, P[mt]);
                 }
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                 zc = 1.0f + 8.0f * (1.0f / MagicConst<MAF>::kInvStep);
               }
     #pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
+              for (int mt = 0; mt < NMT; ++mt)
     #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(sp, __builtin_fmaf(-zc, R[mt][i], P[mt][i]), acc[mt][i]);
             }
@@ -316,9 +327,10 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   RedRow* sRed0 = reinterpret_cast<RedRow*>(sA);
   auto sRed = [&](int p, int row) -> float* { return sRed0[p * BM + row]; };
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sRed(q, 16 * mt + 4 * g + i)[16 * cb + r] = acc[mt][i];
+    for (int i = 0; i < 4; ++i)
+      if (16 * mt + 4 * g + i < BM) sRed(q, 16 * mt + 4 * g + i)[16 * cb + r] = acc[mt][i];
   __syncthreads();
   uint16_t* yb = (uint16_t*)a.y;
   constexpr int BN = NCB * 16;
@@ -353,6 +365,7 @@ static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) 
   constexpr int KQ = (WP == WP_FP8) ? 8 : 4;
   if (t.ncb != NCB || t.kq != KQ) return false;
   switch (t.mt) {
+    case 0: launch_one<WP, AF, OF, ST, ZERO, 0, NCB, KQ, MOE>(a, t, st); return true;
     case 1: launch_one<WP, AF, OF, ST, ZERO, 1, NCB, KQ, MOE>(a, t, st); return true;
     case 2: launch_one<WP, AF, OF, ST, ZERO, 2, NCB, KQ, MOE>(a, t, st); return true;
     case 4: launch_one<WP, AF, OF, ST, ZERO, 4, NCB, KQ, MOE>(a, t, st); return true;

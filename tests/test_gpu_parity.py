@@ -86,7 +86,7 @@ def test_dense_w4a16_sym_f16_full_size(m):
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 15, 16, 17, 31, 33, 64, 100, 129])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 15, 16, 17, 31, 33, 64, 100, 129])
 def test_dense_w4a16_asym_bf16_ragged_m(m):
     layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=320, k=1280, seed=3)
     y = _run_dense(layer, acts, m)
