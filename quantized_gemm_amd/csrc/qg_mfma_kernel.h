@@ -330,25 +330,36 @@ void mfma_gemm_kernel(MfmaArgs a) {
     for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(scl[S1][t]), "+v"(zsl[S1][t]));
 
     if constexpr (F8) {
+      // 2 x MT MFMA pairs per step (k halves j, row tiles mt); each pair's activation
+      // fragment is read two pairs ahead, and sched_barrier keeps the compiler from
+      // hoisting every read (that would need 16 more fragments live).
+      auto read_a8 = [&](int q) -> i32x8 {
+        const int j = q / MT, mt = q % MT;
+        const int row = 32 * (MT * wm + mt) + r;
+        const int lc0 = 4 * g + 2 * j;
+        const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
+        const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
+        i32x8 A;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+        for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
+        return A;
+      };
+      constexpr int NQ = 2 * MT;
+      i32x8 Af8[3];
+      Af8[0] = read_a8(0);
+      Af8[1] = read_a8(1);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int j = q / MT, mt = q % MT;
+        if (q + 2 < NQ) Af8[(q + 2) % 3] = read_a8(q + 2);
         i32x8 B[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) { B[t][i] = (int)b0[t][2 * j][i]; B[t][4 + i] = (int)b0[t][2 * j + 1][i]; }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int row = 32 * (MT * wm + mt) + r;
-          const int lc0 = 4 * g + 2 * j;
-          const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
-          const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
-          i32x8 A;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x64_fp8(A, B[t], acc[mt][t]);
-        }
+        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       // Software pipeline over the 4 sub-steps, ordered by hand: after the two MFMAs of
@@ -471,7 +482,7 @@ static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // 256-row tiles run as 8 waves (2 row halves x 4 column quarters, 2 waves per SIMD)
   constexpr int MW = 1;
   // two waves per SIMD: one workgroup of 8 waves (256 rows) or two workgroups of 4 (128 rows)
-  static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles");
+  static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles (256 rows spill)");
   constexpr int OCC = (WP == WP_FP8 || BM == 256) ? 1 : 2;   // 256x64 / fp8 wave tiles need > 256 registers
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, MW, OCC>), grid, dim3(256 * MW), 0, st, a);
 }
