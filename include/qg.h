@@ -138,6 +138,13 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
 /*
  * qg_workspace_bytes: device workspace qg_gemm / qg_moe_gemm need for m rows
  * (dense) or T tokens x topk (MoE; pass topk = 0 for dense).  0 means none.
+ *   - dense shapes whose output tiles fill at most half the GPU split K over
+ *     workgroups: ksplit * m * N * 4 bytes of fp32 partial sums (required:
+ *     QG_ERR_WORKSPACE without it);
+ *   - W4A8 layers (int4 -> e4m3 compute) above the weight-streaming sizes: the
+ *     activations widened to bf16, rows * K * 2 bytes.  Optional: with it the
+ *     product runs on the 16-bit MFMA path (exact widening, per-token scale in the
+ *     epilogue), without it on the e4m3 MFMA path.
  */
 size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk);
 

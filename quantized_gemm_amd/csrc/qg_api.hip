@@ -233,9 +233,28 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   return t;
 }
 
-// Workspace of a dense call: the split-K partial sums.
+// W4A8 above the streaming sizes: with a workspace for the activations widened to bf16,
+// the 16-bit MFMA kernel runs the product (QUAD int4 decoded exactly to bf16, per-token
+// scale in its epilogue); without one, the e4m3 MFMA kernel with per-group promotion.
+bool is_w4a8(const PathInfo& pi) { return pi.wp_small == WP_INT4Q_MAGIC; }
+size_t widened_bytes(const qg_prepared* p, int64_t rows) {
+  return ((size_t)rows * (size_t)p->desc.k * 2 + 255) / 256 * 256;
+}
+bool widen_ok(const qg_prepared* p, int64_t rows, const void* ws, size_t ws_bytes) {
+  const size_t need = widened_bytes(p, rows);
+  return ws && aligned16(ws) && ws_bytes >= need && need < ((size_t)1 << 31);   // one buffer resource
+}
+PathInfo widened_path(const PathInfo& pi) {
+  PathInfo w = pi;
+  w.wp_mfma = WP_INT4Q_MAGIC;
+  w.af = A_BF16;
+  return w;
+}
+
+// Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
   if (m <= kStreamMaxRows) return 0;
+  if (is_w4a8(pi)) return widened_bytes(p, m);
   const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
   return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
 }
@@ -304,7 +323,9 @@ size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t top
   PathInfo pi;
   if (check_prepared(p, &pi) != QG_OK || m_or_tokens <= 0) return 0;
   if (topk == 0 && p->desc.num_experts == 1) return dense_workspace(p, pi, m_or_tokens);
-  return 0;   // the grouped (MoE) kernels need none
+  if (topk > 0 && is_w4a8(pi) && qg_moe_block_m(p, m_or_tokens, topk) > kStreamMaxRows)
+    return widened_bytes(p, m_or_tokens);          // the tokens' activations, widened
+  return 0;
 }
 
 static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
@@ -344,6 +365,18 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
+  if (m > kStreamMaxRows && is_w4a8(pi) && widen_ok(p, m, ws, ws_bytes)) {
+    const PathInfo pw = widened_path(pi);
+    MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pw);
+    t.ksplit = 1;
+    launch_widen_e4m3_bf16(x, ws, m * p->desc.k, (hipStream_t)stream);
+    a.x = ws;
+    QG_LOG("gemm m=%lld n=%lld k=%lld -> widened e4m3, mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
+           (long long)p->desc.k, t.bm, t.grid_x);
+    if (!launch_mfma_gemm(a, t, pw.wp_mfma, pw.af, pw.of, pw.st, false, false, (hipStream_t)stream))
+      return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
   if (m > kStreamMaxRows) {
     const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
     if (t.ksplit > 1) {
@@ -422,7 +455,6 @@ qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, in
 qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
                       const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
                       int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   PathInfo pi;
   qg_status s = check_prepared(p, &pi);
   if (s != QG_OK) return s;
@@ -449,6 +481,16 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     t.bm = block_m;
     t.grid_x = (unsigned)((p->desc.n + 255) / 256);
     t.grid_y = (unsigned)cb;
+    if (is_w4a8(pi) && widen_ok(p, tokens, ws, ws_bytes)) {
+      const PathInfo pw = widened_path(pi);
+      launch_widen_e4m3_bf16(x, ws, tokens * p->desc.k, (hipStream_t)stream);
+      a.x = ws;
+      QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> widened e4m3, mfma grid=%ux%u", (long long)tokens, topk, block_m,
+             t.grid_x, t.grid_y);
+      if (!launch_mfma_gemm(a, t, pw.wp_mfma, pw.af, pw.of, pw.st, false, true, (hipStream_t)stream))
+        return QG_ERR_UNSUPPORTED;
+      return launched();
+    }
     QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> mfma grid=%ux%u", (long long)tokens, topk, block_m, t.grid_x, t.grid_y);
     if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
       return QG_ERR_UNSUPPORTED;

@@ -41,6 +41,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int NS = 3;                      // activation stages in LDS (ring)
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
   constexpr int BU = F8 ? 4 : 1;             // 16-byte weight units per lane per tile and step
+  // elements held by the bytes of the low / high nibble words of a 4-bit code word
+  constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
+  constexpr int M0[4] = {0, QUAD ? 1 : 4, QUAD ? 2 : 1, QUAD ? 3 : 5};
+  constexpr int M1[4] = {QUAD ? 4 : 2, QUAD ? 5 : 6, QUAD ? 6 : 3, 7};
 
   // one array per stage: the compiler then sees which stage an LDS read and an
   // HBM->LDS load touch, and waits only where they really overlap
@@ -179,7 +183,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
         const int64_t gi = (int64_t)(kstep0 + step) * 2 + g;   // group 32 == unit
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         zs[t] = 0.f;
-      } else if constexpr (WP == WP_INT4_MAGIC) {
+      } else if constexpr (WP == WP_INT4_MAGIC || WP == WP_INT4Q_MAGIC) {
         const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         float z = 8.0f;
@@ -244,20 +248,24 @@ void mfma_gemm_kernel(MfmaArgs a) {
       if constexpr (WP == WP_FP4) {
         Bq[t] = fp4_to_16<AF>(w, sc[t]);
       } else {
-        // PAIR nibble order: bytes of x0 hold elements (0,4,1,5), bytes of x1 (2,6,3,7).
-        // The empty asm hides where x0/x1 come from so that each byte converts with a
-        // single v_cvt_f32_ubyteN instead of a bit-field extract plus a conversion.
-        uint32_t x0 = w & 0x0F0F0F0Fu, x1 = (w >> 4) & 0x0F0F0F0Fu;
+        // PAIR nibble order (biased u = q + 8 or uint4): bytes of x0 hold elements
+        // (0,4,1,5), bytes of x1 (2,6,3,7).  QUAD order (two's complement int4, XOR-ed to
+        // q + 8 here): bytes of x0 hold elements 0..3, of x1 4..7.  The empty asm hides
+        // where x0/x1 come from so that each byte converts with a single
+        // v_cvt_f32_ubyteN instead of a bit-field extract plus a conversion.
+        const uint32_t wb = WP == WP_INT4Q_MAGIC ? (w ^ 0x88888888u) : w;
+        uint32_t x0 = wb & 0x0F0F0F0Fu, x1 = (wb >> 4) & 0x0F0F0F0Fu;
         asm volatile("" : "+v"(x0), "+v"(x1));
-        const float e0 = __builtin_fmaf((float)(x0 & 0xFF), sc[t], zs[t]);
-        const float e4 = __builtin_fmaf((float)((x0 >> 8) & 0xFF), sc[t], zs[t]);
-        const float e1 = __builtin_fmaf((float)((x0 >> 16) & 0xFF), sc[t], zs[t]);
-        const float e5 = __builtin_fmaf((float)(x0 >> 24), sc[t], zs[t]);
-        const float e2 = __builtin_fmaf((float)(x1 & 0xFF), sc[t], zs[t]);
-        const float e6 = __builtin_fmaf((float)((x1 >> 8) & 0xFF), sc[t], zs[t]);
-        const float e3 = __builtin_fmaf((float)((x1 >> 16) & 0xFF), sc[t], zs[t]);
-        const float e7 = __builtin_fmaf((float)(x1 >> 24), sc[t], zs[t]);
-        Bq[t] = u32x4{pack2<AF>(e0, e1), pack2<AF>(e2, e3), pack2<AF>(e4, e5), pack2<AF>(e6, e7)};
+        float e[8];
+        e[M0[0]] = __builtin_fmaf((float)(x0 & 0xFF), sc[t], zs[t]);
+        e[M0[1]] = __builtin_fmaf((float)((x0 >> 8) & 0xFF), sc[t], zs[t]);
+        e[M0[2]] = __builtin_fmaf((float)((x0 >> 16) & 0xFF), sc[t], zs[t]);
+        e[M0[3]] = __builtin_fmaf((float)(x0 >> 24), sc[t], zs[t]);
+        e[M1[0]] = __builtin_fmaf((float)(x1 & 0xFF), sc[t], zs[t]);
+        e[M1[1]] = __builtin_fmaf((float)((x1 >> 8) & 0xFF), sc[t], zs[t]);
+        e[M1[2]] = __builtin_fmaf((float)((x1 >> 16) & 0xFF), sc[t], zs[t]);
+        e[M1[3]] = __builtin_fmaf((float)(x1 >> 24), sc[t], zs[t]);
+        Bq[t] = u32x4{pack2<AF>(e[0], e[1]), pack2<AF>(e[2], e[3]), pack2<AF>(e[4], e[5]), pack2<AF>(e[6], e[7])};
       }
     }
   };
@@ -275,19 +283,20 @@ void mfma_gemm_kernel(MfmaArgs a) {
       out[stg] = (AF == A_F16) ? fp4_to_16<A_F16>(w, sc[t])[stg] : fp4_to_16<A_BF16>(w, sc[t])[stg];
     } else {
       if (stg == 0) {
-        d.x0 = w & 0x0F0F0F0Fu;
-        d.x1 = (w >> 4) & 0x0F0F0F0Fu;
+        const uint32_t wb = WP == WP_INT4Q_MAGIC ? (w ^ 0x88888888u) : w;
+        d.x0 = wb & 0x0F0F0F0Fu;
+        d.x1 = (wb >> 4) & 0x0F0F0F0Fu;
         asm volatile("" : "+v"(d.x0), "+v"(d.x1));   // keep v_cvt_f32_ubyteN (see dequant)
       } else if (stg == 1) {
-        d.e[0] = __builtin_fmaf((float)(d.x0 & 0xFF), sc[t], zs[t]);
-        d.e[4] = __builtin_fmaf((float)((d.x0 >> 8) & 0xFF), sc[t], zs[t]);
-        d.e[1] = __builtin_fmaf((float)((d.x0 >> 16) & 0xFF), sc[t], zs[t]);
-        d.e[5] = __builtin_fmaf((float)(d.x0 >> 24), sc[t], zs[t]);
+        d.e[M0[0]] = __builtin_fmaf((float)(d.x0 & 0xFF), sc[t], zs[t]);
+        d.e[M0[1]] = __builtin_fmaf((float)((d.x0 >> 8) & 0xFF), sc[t], zs[t]);
+        d.e[M0[2]] = __builtin_fmaf((float)((d.x0 >> 16) & 0xFF), sc[t], zs[t]);
+        d.e[M0[3]] = __builtin_fmaf((float)(d.x0 >> 24), sc[t], zs[t]);
       } else if (stg == 2) {
-        d.e[2] = __builtin_fmaf((float)(d.x1 & 0xFF), sc[t], zs[t]);
-        d.e[6] = __builtin_fmaf((float)((d.x1 >> 8) & 0xFF), sc[t], zs[t]);
-        d.e[3] = __builtin_fmaf((float)((d.x1 >> 16) & 0xFF), sc[t], zs[t]);
-        d.e[7] = __builtin_fmaf((float)(d.x1 >> 24), sc[t], zs[t]);
+        d.e[M1[0]] = __builtin_fmaf((float)(d.x1 & 0xFF), sc[t], zs[t]);
+        d.e[M1[1]] = __builtin_fmaf((float)((d.x1 >> 8) & 0xFF), sc[t], zs[t]);
+        d.e[M1[2]] = __builtin_fmaf((float)((d.x1 >> 16) & 0xFF), sc[t], zs[t]);
+        d.e[M1[3]] = __builtin_fmaf((float)(d.x1 >> 24), sc[t], zs[t]);
       } else {
         out = u32x4{pack2<AF>(d.e[0], d.e[1]), pack2<AF>(d.e[2], d.e[3]), pack2<AF>(d.e[4], d.e[5]),
                     pack2<AF>(d.e[6], d.e[7])};
@@ -449,7 +458,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
             *(float*)(ep + rl * PITCH + (32 * t + r) * 4) = v;
           } else {
             v *= sw[t];
-            if constexpr (AF == A_FP8) {
+            if constexpr (AF == A_FP8 || WP == WP_INT4Q_MAGIC) {   // per-token scale (e4m3 activations)
               const int tok = sRowTok[rbase + rl];
               v *= tok < 0 ? 0.f : a.x_scale[tok];
             }

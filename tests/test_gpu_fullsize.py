@@ -87,7 +87,8 @@ def _moe_check(layer, acts, seed):
     qg.moe_align(ids, t, topk, layer.experts, bm, sid, eid, npp)
     x, xs = layers.acts_to_dev(acts)
     y = torch.full((t * topk, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
-    qg.moe_gemm(p, x, xs, sid, eid, npp, t, topk, bm, y)
+    ws = torch.zeros(max(1, qg.workspace_bytes(p, t, topk)), dtype=torch.uint8, device="cuda")
+    qg.moe_gemm(p, x, xs, sid, eid, npp, t, topk, bm, y, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all()), "non-finite output"
     rng = np.random.default_rng(seed)

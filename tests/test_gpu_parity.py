@@ -163,14 +163,17 @@ def test_moe_align_is_bit_exact(case):
     assert np.array_equal(e.cpu().numpy(), re_)
 
 
-def _run_moe(layer, acts):
+def _run_moe(layer, acts, workspace=False):
     t, topk = acts.topk_ids.shape
     p, buf = layers.prepare_layer(layer)
     bm = qg.moe_block_m(p, t, topk)
     s, e, n = _align_gpu(acts.topk_ids, layer.experts, bm)
     x, xs = layers.acts_to_dev(acts)
     y = torch.full((t * topk, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
-    qg.moe_gemm(p, x, xs, s, e, n, t, topk, bm, y)
+    ws = None
+    if workspace:
+        ws = torch.zeros(max(1, qg.workspace_bytes(p, t, topk)), dtype=torch.uint8, device="cuda")
+    qg.moe_gemm(p, x, xs, s, e, n, t, topk, bm, y, ws)
     torch.cuda.synchronize()
     return layers.out_bits_to_f64(y).reshape(t, topk, layer.n)
 
@@ -292,3 +295,26 @@ def test_dense_split_k_is_deterministic_and_checks_workspace():
         qg.gemm(p, x, None, y1, 96, ws[: need - 16])
     with pytest.raises(qg.QGError):
         qg.gemm(p, x, None, y1, 96, None)
+
+
+# ---- W4A8 above the streaming sizes: both routes ---------------------------------------
+# With the workspace qg_workspace_bytes asks for, the e4m3 activations are widened to bf16
+# and the 16-bit MFMA kernel runs; without it, the e4m3 MFMA kernel with per-group promotion.
+
+@pytest.mark.parametrize("m", [100, 300])
+def test_dense_w4a8_without_workspace_runs_e4m3_mfma(m):
+    layer, acts = synth.moe_w4a8_int4(t=m, experts=1, topk=1, n=320, k=1024, seed=17)
+    p, buf = layers.prepare_layer(layer)
+    assert qg.workspace_bytes(p, m) == ((m * 1024 * 2 + 255) // 256) * 256
+    x, xs = layers.acts_to_dev(acts)
+    y = torch.full((m, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
+    qg.gemm(p, x, xs, y, m, None)
+    torch.cuda.synchronize()
+    assert R.relative_error(layers.out_bits_to_f64(y), R.dense_reference(layer, acts)) <= TOL8
+
+
+@pytest.mark.parametrize("t", [400, 1000])
+def test_moe_w4a8_int4_widened_route(t):
+    layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=18)
+    y = _run_moe(layer, acts, workspace=True)
+    assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
