@@ -358,12 +358,11 @@ static void launch_one(const StreamArgs& a, const StreamTile& t, hipStream_t st)
                      dim3(64 * NCB * KQ), 0, st, a);
 }
 
-// Shapes: (NCB, KQ) = (2, 4) for 4-bit weights, (1, 8) for e4m3 weights.
-template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE>
-static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
-  constexpr int NCB = (WP == WP_FP8) ? 1 : 2;
-  constexpr int KQ = (WP == WP_FP8) ? 8 : 4;
-  if (t.ncb != NCB || t.kq != KQ) return false;
+// Shapes: (NCB, KQ) = (2, 4) for 4-bit weights, (1, 8) for e4m3 weights; MoE blocks of
+// 16..64 rows with 4-bit weights also (8, 1): 128 columns per workgroup, so a block's
+// activation rows are staged by 4x fewer workgroups (the grid has blocks to spare).
+template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE, int NCB, int KQ>
+static bool launch_shape(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
   switch (t.mt) {
     case 0: launch_one<WP, AF, OF, ST, ZERO, 0, NCB, KQ, MOE>(a, t, st); return true;
     case 1: launch_one<WP, AF, OF, ST, ZERO, 1, NCB, KQ, MOE>(a, t, st); return true;
@@ -371,6 +370,18 @@ static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) 
     case 4: launch_one<WP, AF, OF, ST, ZERO, 4, NCB, KQ, MOE>(a, t, st); return true;
     default: return false;
   }
+}
+
+template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE>
+static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
+  if constexpr (WP == WP_FP8) {
+    if (t.ncb == 1 && t.kq == 8) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 1, 8>(a, t, st);
+  } else {
+    if (t.ncb == 2 && t.kq == 4) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 2, 4>(a, t, st);
+    if constexpr (MOE)
+      if (t.ncb == 8 && t.kq == 1 && t.mt >= 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
+  }
+  return false;
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
