@@ -497,7 +497,7 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     return launched();
   }
   StreamTile t = stream_tile(block_m, p->desc.n, p->desc.w_type);
-  if (block_m >= 16 && p->desc.w_type != QG_W_FP8_E4M3) {   // 128 columns per workgroup (see launch_mt)
+  if (p->desc.w_type != QG_W_FP8_E4M3) {   // 128 columns per workgroup (see launch_mt)
     t.ncb = 8;
     t.kq = 1;
     t.grid_x = (unsigned)((p->desc.n / 16 + 7) / 8);

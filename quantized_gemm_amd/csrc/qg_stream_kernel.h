@@ -358,9 +358,10 @@ static void launch_one(const StreamArgs& a, const StreamTile& t, hipStream_t st)
                      dim3(64 * NCB * KQ), 0, st, a);
 }
 
-// Shapes: (NCB, KQ) = (2, 4) for 4-bit weights, (1, 8) for e4m3 weights; MoE blocks of
-// 16..64 rows with 4-bit weights also (8, 1): 128 columns per workgroup, so a block's
-// activation rows are staged by 4x fewer workgroups (the grid has blocks to spare).
+// Shapes: (NCB, KQ) = (2, 4) for 4-bit weights, (1, 8) for e4m3 weights; MoE blocks with
+// 4-bit weights (8, 1): 128 columns per workgroup, so a block's activation rows are staged
+// by 4x fewer workgroups and no K parts need adding (the grid has blocks to spare; a dense
+// layer needs the K parts to fill the GPU).
 template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE, int NCB, int KQ>
 static bool launch_shape(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
   switch (t.mt) {
@@ -379,7 +380,7 @@ static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) 
   } else {
     if (t.ncb == 2 && t.kq == 4) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 2, 4>(a, t, st);
     if constexpr (MOE)
-      if (t.ncb == 8 && t.kq == 1 && t.mt >= 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
+      if (t.ncb == 8 && t.kq == 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
   }
   return false;
 }
