@@ -251,9 +251,28 @@ PathInfo widened_path(const PathInfo& pi) {
   return w;
 }
 
+// Dense weight streaming for 5..64 rows: workgroups of 8 column blocks (128 columns) x 1 K
+// part, with K split over up to 8 workgroups so that about one workgroup per CU remains.
+// Each workgroup then stages only its slice of K for its rows (one LDS round at 16 rows)
+// instead of all of K; the fp32 partials are summed by the split-K reduction.  1..4 rows
+// keep the 2 x 4 shape without a split (their 4-row staging is already one round).
+int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
+  if (rows <= 4) return 1;
+  const int64_t groups = (n / 16 + 7) / 8;
+  const int64_t chunks = k / 128;
+  int sp = 1;
+  while (sp < 8 && groups * sp * 2 <= kCUs && chunks % (sp * 2) == 0 &&
+         (group <= 0 || (k / (sp * 2)) % group == 0))
+    sp *= 2;
+  return sp;
+}
+
 // Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
-  if (m <= kStreamMaxRows) return 0;
+  if (m <= kStreamMaxRows) {
+    const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
+    return sp > 1 ? (size_t)sp * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
+  }
   if (is_w4a8(pi)) return widened_bytes(p, m);
   const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
   return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
@@ -394,10 +413,22 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
       return QG_ERR_UNSUPPORTED;
     return launched();
   }
-  const StreamTile t = stream_tile(m, p->desc.n, p->desc.w_type);
-  QG_LOG("gemm m=%lld n=%lld k=%lld -> stream mt=%d grid=%ux%u", (long long)m, (long long)p->desc.n,
-         (long long)p->desc.k, t.mt, t.grid_x, t.grid_y);
+  StreamTile t = stream_tile(m, p->desc.n, p->desc.w_type);
+  const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
+  if (sp > 1) {
+    const size_t need = dense_workspace(p, pi, m);
+    if (!ws || !aligned16(ws) || ws_bytes < need) return QG_ERR_WORKSPACE;
+    t.ncb = 8;
+    t.kq = 1;
+    t.grid_x = (unsigned)((p->desc.n / 16 + 7) / 8);
+    a.part = (float*)ws;
+    a.ksplit = sp;
+  }
+  QG_LOG("gemm m=%lld n=%lld k=%lld -> stream mt=%d grid=%ux%ux%d", (long long)m, (long long)p->desc.n,
+         (long long)p->desc.k, t.mt, t.grid_x, t.grid_y, sp);
   if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  if (sp > 1 && !launch_split_reduce(a, pi.wp_small == WP_FP8, pi.af == A_FP8, pi.of, (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();
 }

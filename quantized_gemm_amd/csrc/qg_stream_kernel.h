@@ -105,7 +105,11 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   const int nb_count = a.n >> 4;
   const int nbw = blockIdx.x * NCB + cb;                 // this wave's 16-column block
   const bool wact = nbw < nb_count;                      // waves past N only help with staging
-  const int nchunks = a.k >> 7;
+  // Dense split K (a.ksplit > 1): workgroup z owns chunks [cbase, cbase + nchunks) of K
+  // (whole scale groups, chosen by the host) and writes fp32 partial sums.
+  const int ksl = (!MOE && a.ksplit > 1) ? a.ksplit : 1;
+  const int nchunks = (a.k >> 7) / ksl;
+  const int cbase = ksl > 1 ? (int)blockIdx.z * nchunks : 0;
   const int per = (nchunks + KQ - 1) / KQ;               // chunks per K part
   const int my0 = q * per;
   const int myn = max(0, min(nchunks, my0 + per) - my0);
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
       const int tok = sRowTok[row];
       const int pn = max(0, min(nchunks, pq * per + per) - pq * per);
       const bool ok = p < APIECES && tok >= 0 && chunk_in_part < pn;
-      const int64_t off = (int64_t)tok * xrow_bytes + (int64_t)(pq * per + rnd * RCR) * 128 * T::ABYTES + 16 * pc;
+      const int64_t off = (int64_t)tok * xrow_bytes + (int64_t)(cbase + pq * per + rnd * RCR) * 128 * T::ABYTES + 16 * pc;
       st.a[i] = bload16(xr, ok ? (int)off : kOOB);
     }
     if constexpr (T::SBYTES > 0) {
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
       const int64_t nb = (int64_t)blockIdx.x * NCB + scb;
       const int chunk_in_part = rnd * RCR + sc;
       const int pn = max(0, min(nchunks, spq * per + per) - spq * per);
-      const int ch = spq * per + chunk_in_part;
+      const int ch = cbase + spq * per + chunk_in_part;
       const bool ok = tid < SPIECES && nb < nb_count && chunk_in_part < pn;
       int64_t elem;
       if constexpr (WP == WP_FP4) elem = (((int64_t)expert * nb_count + nb) * ngroups + (int64_t)ch * 4) * 16;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
         const int64_t znb = (int64_t)blockIdx.x * NCB + zcb;
         const int zcp = rnd * RCR + zc;
         const int zpn = max(0, min(nchunks, zpq * per + per) - zpq * per);
-        const int zch = zpq * per + zcp;
+        const int zch = cbase + zpq * per + zcp;
         const bool zok = tid < ZSLOTS && znb < nb_count && zcp < zpn;
         const int grp = a.group == 0 ? 0 : (zch * 128) / a.group;
         st.z = bload8(zr, zok ? (int)(((((int64_t)expert * nb_count + znb) * ngroups + grp) << 1) * 4) : kOOB);
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     u32x4 bw[CHMAX][T::B_U4];
 #pragma unroll
     for (int c = 0; c < CHMAX; ++c) {
-      const int ch = my0 + b0 + c;
+      const int ch = cbase + my0 + b0 + c;
 #pragma unroll
       for (int u = 0; u < T::B_U4; ++u) {
         const int64_t ku = T::kFp8Mfma ? ((int64_t)ch * 8 + 2 * g + u) : ((int64_t)ch * 4 + g);
@@ -342,6 +346,10 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     float v = 0.f;
 #pragma unroll
     for (int p = 0; p < KQ; ++p) v += sRed(p, row)[col];
+    if (ksl > 1) {                                    // partial sum of this K slice, unscaled
+      a.part[((int64_t)blockIdx.z * a.m + rowbase + row) * a.n + n] = v;
+      continue;
+    }
     if constexpr (WP == WP_FP8) v *= ((const float*)a.s)[(int64_t)expert * a.n + n];
     if constexpr (AF == A_FP8) v *= a.x_scale[tok];
     int64_t orow;
@@ -354,7 +362,8 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
 // ---- launch helpers (instantiated per weight path in qg_stream_*.hip) --------------
 template <int WP, int AF, int OF, int ST, bool ZERO, int MT, int NCB, int KQ, bool MOE>
 static void launch_one(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
-  hipLaunchKernelGGL((stream_gemm_kernel<WP, AF, OF, ST, ZERO, MT, NCB, KQ, MOE>), dim3(t.grid_x, t.grid_y),
+  hipLaunchKernelGGL((stream_gemm_kernel<WP, AF, OF, ST, ZERO, MT, NCB, KQ, MOE>),
+                     dim3(t.grid_x, t.grid_y, a.ksplit > 1 ? a.ksplit : 1),
                      dim3(64 * NCB * KQ), 0, st, a);
 }
 
@@ -377,10 +386,11 @@ template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE>
 static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
   if constexpr (WP == WP_FP8) {
     if (t.ncb == 1 && t.kq == 8) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 1, 8>(a, t, st);
+    if constexpr (!MOE)
+      if (t.ncb == 8 && t.kq == 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
   } else {
     if (t.ncb == 2 && t.kq == 4) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 2, 4>(a, t, st);
-    if constexpr (MOE)
-      if (t.ncb == 8 && t.kq == 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
+    if (t.ncb == 8 && t.kq == 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);
   }
   return false;
 }

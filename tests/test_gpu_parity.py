@@ -318,3 +318,17 @@ def test_moe_w4a8_int4_widened_route(t):
     layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=18)
     y = _run_moe(layer, acts, workspace=True)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
+
+
+def test_dense_streaming_split_needs_workspace():
+    # 16 rows of a 2048-column layer: 16 column groups x 8 K slices of weight streaming
+    layer, acts = synth.dense_w4a16_asym_bf16(m=16, n=2048, k=4096, seed=19)
+    p, buf = layers.prepare_layer(layer)
+    assert qg.workspace_bytes(p, 16) == 8 * 16 * 2048 * 4
+    assert qg.workspace_bytes(p, 4) == 0
+    x, _ = layers.acts_to_dev(acts)
+    y = torch.empty((16, 2048), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(qg.QGError):
+        qg.gemm(p, x, None, y, 16, None)
+    y = _run_dense(layer, acts, 16)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
