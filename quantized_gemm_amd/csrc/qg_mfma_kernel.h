@@ -170,7 +170,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
         const int64_t gs = (int64_t)(kstep0 + step);
         const int64_t ku = F8 ? (gs * 8 + 4 * g + u) : (gs * 2 + g);
         const bool ok = wok[t] && step < nsteps;
-        dst[t][u] = bload16_stream(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
+        // cached: every weight tile is read again by the other row tiles of the XCD
+        dst[t][u] = bload16(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
       }
     }
   };
@@ -215,9 +216,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
   // idle and its registers free for other values.  Vector-memory issue order, kept by
   // sched_barrier: [B(0)] A(0) B(DIST-2) A(1) B(DIST-1), then per step s A(s+2) at the top
-  // and B(s+DIST) at the bottom.  At the top of step s the loads issued after A(s)
-  // include at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <= APT + 2*NB means
-  // A(s) has landed; the scale loads only make that count larger, so the wait is safe.
+  // and B(s+DIST) at the bottom (DIST = 3) or right after A(s+2) (DIST = 2).  At the top of
+  // step s the loads issued after A(s) include at least B(s+DIST-2), A(s+1) and
+  // B(s+DIST-1), so vmcnt <= APT + 2*NB means A(s) has landed; the scale loads only make
+  // that count larger, so the wait is safe.
   constexpr int DIST = F8 ? 2 : 3;
   u32x4 bw[3][NT][BU];
   float scl[3][NT], zsl[3][NT];
@@ -329,6 +331,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
     asm volatile("" ::: "memory");
     issue_a(step + 2, sAn);
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int SL = (S + DIST) % 3;                        // slot of step + DIST
+    if constexpr (DIST == 2) {
+      // e4m3 weights: the slot of step + 2 (last read in step - 1) is free already, so
+      // its loads go out here, two full steps ahead of use, right after A(step + 2)
+      load_b(step + DIST, bw[SL]);
+      load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     auto& b0 = bw[S];
     auto& b1 = bw[S1];
@@ -404,11 +414,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
         }
       }
     }
-    // weights and scales of step + DIST into their slot (DIST = 3: this step's, now free)
-    constexpr int SL = (S + DIST) % 3;
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(step + DIST, bw[SL]);
-    load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
+    // DIST = 3: weights and scales of step + 3 into this step's slot, now free
+    if constexpr (DIST == 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(step + DIST, bw[SL]);
+      load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
+    }
   };
   // The step count is padded to a multiple of three rather than leaving the unrolled
   // loop early (early exits make the accumulators spill).  A padded step reads its
