@@ -26,15 +26,16 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int MW, int OCC>
-__global__ __launch_bounds__(256 * MW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int CW, int OCC>
+__global__ __launch_bounds__(64 * CW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (WP == WP_FP8);
   constexpr int AB = F8 ? 1 : 2;
   constexpr int BK = F8 ? 128 : 64;          // K per step; one LDS row segment = 128 bytes
-  constexpr int NTHR = 256 * MW;             // MW groups of 4 waves split the rows
-  constexpr int MT = BM / 32 / MW;           // 32-row MFMA tiles per wave
-  constexpr int NT = 2;                      // 32-column MFMA tiles per wave
+  constexpr int NTHR = 64 * CW;              // CW waves, each owning BN / CW columns and all BM rows
+  constexpr int MT = BM / 32;                // 32-row MFMA tiles per wave
+  constexpr int WCOL = 256 / CW;             // columns per wave: 64 (4 waves) or 32 (8 waves)
+  constexpr int NT = WCOL / 32;              // 32-column MFMA tiles per wave
   constexpr int BN = 256;
   constexpr int ROWB = 128;
   constexpr int STAGE = BM * ROWB;
@@ -56,8 +57,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // column quarter
-  const int wm = __builtin_amdgcn_readfirstlane(tid >> 8);           // row part
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);         // column slice of the tile
   const int r = lane & 31;
   const int g = lane >> 5;
 
@@ -118,7 +118,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __syncthreads();
 
   const int nb_count = a.n >> 4;
-  const int64_t col0 = (int64_t)ntile * BN + 64 * wave;     // first column of this wave
+  const int64_t col0 = (int64_t)ntile * BN + WCOL * wave;   // first column of this wave
   // Split K: workgroup z owns steps [kstep0, kstep0 + nsteps) and writes fp32 partial
   // sums (the host makes the slices whole scale groups); otherwise all of K.
   const int nsteps = SPLIT ? a.k / BK / a.ksplit : a.k / BK;
@@ -309,7 +309,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   auto read_a16 = [&](const uint8_t* sAb, int j, u32x4 (&Af)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int row = 32 * (MT * wm + mt) + r;
+      const int row = 32 * mt + r;
       Af[mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j) ^ ((row >> 1) & 7)));
     }
   };
@@ -354,7 +354,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // hoisting every read (that would need 16 more fragments live).
       auto read_a8 = [&](int q) -> i32x8 {
         const int j = q / MT, mt = q % MT;
-        const int row = 32 * (MT * wm + mt) + r;
+        const int row = 32 * mt + r;
         const int lc0 = 4 * g + 2 * j;
         const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
         const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
@@ -385,8 +385,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // each row tile come one stage of the next sub-step's dequantization and that tile's
       // next activation fragment read; sched_barrier keeps the order.  Sub-step 3
       // dequantizes sub-step 0 of the next step (its weights and scales are in registers).
-      u32x4 Af[2][MT];
-      read_a16(sAb, 0, Af[0]);
+      // one fragment register set per row tile: a tile's next fragment is read into it
+      // right after its MFMAs, one sub-step (MT * NT MFMAs) ahead of use
+      u32x4 Af[MT];
+      read_a16(sAb, 0, Af);
       constexpr int PH = NT * 4;                 // dequant stages per sub-step
       constexpr int PPM = (PH + MT - 1) / MT;    // stages after each row tile
 #pragma unroll
@@ -396,7 +398,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[j & 1][mt], Bq[j & 1][t], acc[mt][t]);
+          for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[mt], Bq[j & 1][t], acc[mt][t]);
 #pragma unroll
           for (int q = 0; q < PPM; ++q) {
             const int ph = mt * PPM + q;
@@ -407,8 +409,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
             }
           }
           if (!last) {
-            const int row = 32 * (MT * wm + mt) + r;
-            Af[(j + 1) & 1][mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j + 1) ^ ((row >> 1) & 7)));
+            const int row = 32 * mt + r;
+            Af[mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j + 1) ^ ((row >> 1) & 7)));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -441,12 +443,13 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // writes whole row segments with 16-byte stores: 128 bytes per output row (16-bit)
   // or 256 bytes (fp32 split-K partials, unscaled: the reduction applies the scales).
   __syncthreads();                                   // every wave is done with the stages
-  if (!wok[0]) return;                               // n % 64 == 0: all or none of the 64 columns
+  if (!wok[0]) return;                               // n % 64 == 0: all or none of a wave's columns
   constexpr int OB = SPLIT ? 4 : 2;                  // output bytes per element
   constexpr int CR = SPLIT ? 16 : 32;                // rows per staged chunk
-  constexpr int PITCH = 64 * OB + 16;                // padded LDS row
-  static_assert(2 * CR * PITCH <= STAGE, "two waves' chunks per stage array");
-  uint8_t* const ep = (wave < 2 ? sA0 : sA1) + (wave & 1) * CR * PITCH;
+  constexpr int PITCH = WCOL * OB + 16;              // padded LDS row
+  constexpr int PER = STAGE / (CR * PITCH);          // waves' chunks per stage array
+  static_assert(3 * PER >= CW, "every wave's chunk fits in the stage arrays");
+  uint8_t* const ep = (wave < PER ? sA0 : wave < 2 * PER ? sA1 : sA2) + (wave % PER) * CR * PITCH;
   const int64_t col0w = col0;                        // first column of this wave
   float sw[NT];
 #pragma unroll
@@ -456,7 +459,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
-      const int rbase = 32 * (MT * wm + mt) + CR * h;          // first tile row of the chunk
+      const int rbase = 32 * mt + CR * h;          // first tile row of the chunk
       // stage: element (row, col) of the chunk at ep + row * PITCH + col * OB
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -476,8 +479,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
             *(uint16_t*)(ep + rl * PITCH + (32 * t + r) * 2) = f32_to_out<OF>(v);
           }
         }
-      // write: CR rows x 64 * OB bytes = CR * 4 * OB pieces of 16 bytes, 64 per lane pass
-      constexpr int PPR = 64 * OB / 16;                        // pieces per row
+      // write: CR rows x WCOL * OB bytes in pieces of 16 bytes, 64 per lane pass
+      constexpr int PPR = WCOL * OB / 16;                      // pieces per row
 #pragma unroll
       for (int q = 0; q < CR * PPR / 64; ++q) {
         const int pc = lane + 64 * q;
@@ -499,12 +502,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT = false>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
-  // 256-row tiles run as 8 waves (2 row halves x 4 column quarters, 2 waves per SIMD)
-  constexpr int MW = 1;
+  // 16-bit 256-row tiles: 8 waves (two per SIMD) of 256 x 32; otherwise 4 waves of BM x 64
+  constexpr int CW = (WP != WP_FP8 && BM == 256) ? 8 : 4;
   // two waves per SIMD: one workgroup of 8 waves (256 rows) or two workgroups of 4 (128 rows)
   static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles (256 rows spill)");
-  constexpr int OCC = (WP == WP_FP8 || BM == 256) ? 1 : 2;   // 256x64 / fp8 wave tiles need > 256 registers
-  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, MW, OCC>), grid, dim3(256 * MW), 0, st, a);
+  constexpr int OCC = WP == WP_FP8 ? 1 : 2;   // e4m3 wave tiles need > 256 registers
+  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW, OCC>), grid, dim3(64 * CW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
