@@ -46,16 +46,23 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
+// A stored 16-bit or UE8M0 scale (its bits, zero-extended) -> fp32.
+template <int ST>
+__device__ __forceinline__ float scale_bits_to_f32(uint32_t b) {
+  static_assert(ST != S_F32, "fp32 scales are read as floats");
+  if constexpr (ST == S_F16) return f16_bits_to_f32(b);
+  else if constexpr (ST == S_BF16) return bf16_bits_to_f32(b);
+  else {
+    // 2^(e-127); e == 0 is the subnormal 2^-127, e == 255 is NaN.
+    return b == 0 ? __uint_as_float(0x00400000u) : (b == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(b << 23));
+  }
+}
+
 template <int ST>
 __device__ __forceinline__ float scale_to_f32(const void* base, int64_t idx) {
-  if constexpr (ST == S_F16) return f16_bits_to_f32(((const uint16_t*)base)[idx]);
-  else if constexpr (ST == S_BF16) return bf16_bits_to_f32(((const uint16_t*)base)[idx]);
-  else if constexpr (ST == S_F32) return ((const float*)base)[idx];
-  else {
-    uint32_t e = ((const uint8_t*)base)[idx];
-    // 2^(e-127); e == 0 is the subnormal 2^-127, e == 255 is NaN.
-    return e == 0 ? __uint_as_float(0x00400000u) : (e == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e << 23));
-  }
+  if constexpr (ST == S_F32) return ((const float*)base)[idx];
+  else if constexpr (ST == S_UE8M0) return scale_bits_to_f32<ST>(((const uint8_t*)base)[idx]);
+  else return scale_bits_to_f32<ST>(((const uint16_t*)base)[idx]);
 }
 
 // Two floats -> packed 16-bit pair (round to nearest even), low half = lo.

@@ -10,15 +10,17 @@
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
 //     in the epilogue.
 //
-// Tile: BM x 256 per workgroup.  Four waves own the column quarters [64w, 64w+64); a
-// 128-row tile uses 4 waves (one per SIMD, no weight dequantized twice), a 256-row
-// tile uses 8 waves (two row halves, two waves per SIMD) so that one wave's dequant
-// VALU work co-executes with the other wave's MFMAs.  Activations go through
-// LDS, double-buffered, one 128-byte row segment per K step with a 16-byte XOR swizzle
-// by row bits 1..3 (16 consecutive rows read the same logical chunk from 16 distinct
-// banks groups: conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
-// prefetched two K steps ahead.  MFMA 32x32x16 (16-bit) or 32x32x64 (fp8), fp32
-// accumulation.  MoE: rows are gathered through sorted_ids and scattered on store.
+// Tile: BM x 256 per workgroup, CW waves, wave w owning all BM rows of the columns
+// [w 256/CW, (w+1) 256/CW), so that every weight is dequantized exactly once per tile.
+// 16-bit paths use 8 waves of 32 columns (two waves per SIMD: one wave's dequant VALU
+// work co-executes with the other's MFMAs; MoE blocks of 128 rows keep 4 waves of 64),
+// e4m3 uses 4 waves of 64.  Activations go HBM -> LDS directly through a ring of three
+// stages, one 128-byte row segment per K step with a 16-byte XOR swizzle by row bits
+// 1..3 (conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
+// prefetched two or three K steps ahead; the scale and zero records of a step travel
+// with the activations into LDS (two loads per workgroup and step, not one per lane).
+// MFMA 32x32x16 (16-bit) or 32x32x64 (fp8), fp32 accumulation.  MoE: rows are gathered
+// through sorted_ids and scattered on store.
 #pragma once
 
 #include "qg_device.h"
@@ -52,6 +54,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sA2[STAGE];
+  // 16-bit paths: the next step's scale (and zero) records of the tile's 256 columns,
+  // one region per activation stage, loaded HBM -> LDS with that stage's activations
+  // (scales in the first KiB, zero words in the second)
+  constexpr bool SDMA = !F8;
+  constexpr int SREG = SDMA ? 2048 : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sS0[SREG];
+  __shared__ __attribute__((aligned(16))) uint8_t sS1[SREG];
+  __shared__ __attribute__((aligned(16))) uint8_t sS2[SREG];
   __shared__ int sRowTok[BM];
   __shared__ int sRowOut[BM];    // output row of each tile row (-1: none)
 
@@ -152,6 +162,58 @@ void mfma_gemm_kernel(MfmaArgs a) {
                   a_off[i] < 0 || step >= nsteps ? kOOB : a_off[i] + (kstep0 + step) * ROWB);
   };
 
+  // ---- scale and zero records: 16 bytes per lane, one load on wave 0 (scales) and one
+  // on wave 1 (zeros) per step instead of one per lane and tile.  Group of K half h of
+  // step t (k = 64t + 32h ..): e2m1 blocks of 32, two per step; int4 groups are a
+  // multiple of 128 (or the whole K), so both halves share one (a wave-uniform division).
+  constexpr int ES = ST == S_UE8M0 ? 1 : 2;               // bytes per stored scale
+  auto group_of = [&](int t, int h) -> int {
+    if constexpr (WP == WP_FP4) return (kstep0 + t) * 2 + h;
+    else return a.group == 0 ? 0 : ((kstep0 + t) * BK) / a.group;
+  };
+  // scale lane -> K half, 16-column block of the tile, 16-byte part of the block's 16 scales
+  const int s_h = lane / (16 * ES), s_nb = (lane % (16 * ES)) / ES, s_part = lane % ES;
+  const bool s_ok = lane < 32 * ES && ntile * 16 + s_nb < nb_count;
+  const bool z_ok = lane < 16 && ntile * 16 + lane < nb_count;   // zero lane -> column block
+  const int64_t sc_expert = (int64_t)expert * nb_count * ngroups;  // records before this expert
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc((const uint8_t*)a.s + sc_expert * 16 * ES, (uint32_t)(nb_count * ngroups * 16 * ES));
+  const __amdgpu_buffer_rsrc_t zr =
+      make_rsrc(ZERO ? (const void*)(a.z + sc_expert * 2) : a.s, ZERO ? (uint32_t)(nb_count * ngroups * 8) : 0u);
+  // Step t's records into region reg: scales of half h at reg + 256 ES h + 16 ES nb + ES c;
+  // the two zero words of the step's group (and the next group's) at reg + 1024 + 16 nb.
+  auto issue_sz = [&](int t, uint8_t* reg) {
+    if constexpr (SDMA) {
+      if (wave == 0) {
+        bload16_lds(sr, reg, s_ok && t < nsteps ? ((ntile * 16 + s_nb) * ngroups + group_of(t, s_h)) * 16 * ES + 16 * s_part
+                                                : kOOB);
+      } else if (ZERO && wave == 1) {
+        bload16_lds(zr, reg + 1024, z_ok && t < nsteps ? ((ntile * 16 + lane) * ngroups + group_of(t, 0)) * 8 : kOOB);
+      }
+    }
+  };
+  // this lane's scale and z * scale for tile column 32 tt + r, from region reg
+  auto read_sz = [&](const uint8_t* reg, float (&s)[NT], float (&zs)[NT]) {
+    if constexpr (SDMA) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int cl = WCOL * wave + 32 * tt + r, nbl = cl >> 4, c = cl & 15;
+      const uint8_t* sp = reg + 256 * ES * g + 16 * ES * nbl + ES * c;
+      s[tt] = scale_bits_to_f32<ST>(ES == 1 ? (uint32_t)*sp : (uint32_t)*(const uint16_t*)sp);
+      if constexpr (WP == WP_FP4) {
+        zs[tt] = 0.f;
+      } else {
+        float z = 8.0f;
+        if constexpr (ZERO) {
+          const uint32_t zw = *(const uint32_t*)(reg + 1024 + 16 * nbl + 4 * (c >> 3));
+          z = (float)((zw >> ((c & 7) * 4)) & 0xF);
+        }
+        zs[tt] = -z * s[tt];
+      }
+    }
+    }
+  };
+
   // ---- weights: per tile t, this lane's column and 16-byte units for a step ----------
   int64_t wcol[NT];
   bool wok[NT];
@@ -215,28 +277,32 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // activations: DIST = 3, since the last sub-step of step s already dequantizes step
   // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
   // idle and its registers free for other values.  Vector-memory issue order, kept by
-  // sched_barrier: [B(0)] A(0) B(DIST-2) A(1) B(DIST-1), then per step s A(s+2) at the top
-  // and B(s+DIST) at the bottom (DIST = 3) or right after A(s+2) (DIST = 2).  At the top of
-  // step s the loads issued after A(s) include at least B(s+DIST-2), A(s+1) and
-  // B(s+DIST-1), so vmcnt <= APT + 2*NB means A(s) has landed; the scale loads only make
-  // that count larger, so the wait is safe.
+  // sched_barrier: [B(0)] R(1) A(0) B(DIST-2) R(2) A(1) B(DIST-1), then per step s R(s+3)
+  // A(s+2) at the top and B(s+DIST) at the bottom (DIST = 3) or right after A(s+2)
+  // (DIST = 2).  R(t) are the scale / zero records of step t (16-bit paths; one load on
+  // waves 0 and 1 only), issued with A(t-1) into that stage's region, so they land when
+  // A(t-1) does and are read at the top of step t-1.  At the top of step s the loads
+  // issued after A(s) include at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <=
+  // APT + 2*NB means A(s) has landed; the record loads only make that count larger.
   constexpr int DIST = F8 ? 2 : 3;
   u32x4 bw[3][NT][BU];
   float scl[3][NT], zsl[3][NT];
   if constexpr (DIST == 3) {
     load_b(0, bw[0]);
-    load_scale(0, scl[0], zsl[0]);
+    load_scale(0, scl[0], zsl[0]);           // later steps' scales come through LDS
     __builtin_amdgcn_sched_barrier(0);
   }
+  issue_sz(1, sS0);
   issue_a(0, sA0);
   __builtin_amdgcn_sched_barrier(0);
   load_b(DIST - 2, bw[DIST - 2]);
-  load_scale(min(DIST - 2, nsteps - 1), scl[DIST - 2], zsl[DIST - 2]);
+  if constexpr (F8) load_scale(min(DIST - 2, nsteps - 1), scl[DIST - 2], zsl[DIST - 2]);
   __builtin_amdgcn_sched_barrier(0);
+  issue_sz(2, sS1);
   issue_a(1, sA1);
   __builtin_amdgcn_sched_barrier(0);
   load_b(DIST - 1, bw[DIST - 1]);
-  load_scale(min(DIST - 1, nsteps - 1), scl[DIST - 1], zsl[DIST - 1]);
+  if constexpr (F8) load_scale(min(DIST - 1, nsteps - 1), scl[DIST - 1], zsl[DIST - 1]);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int NB = NT * BU;                // weight loads per thread per step
   constexpr int VM_A = APT + 2 * NB;
@@ -323,12 +389,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
     constexpr int S = decltype(S_)::value;
     uint8_t* const sAb = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
     uint8_t* const sAn = S == 0 ? sA2 : S == 1 ? sA0 : sA1;   // stage of step + 2
+    const uint8_t* const sSb = S == 0 ? sS0 : S == 1 ? sS1 : sS2;
+    uint8_t* const sSn = S == 0 ? sS2 : S == 1 ? sS0 : sS1;
     // this wave's A(step) loads have landed; the barrier makes every wave's visible and
     // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
     __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_A & 15) | ((VM_A >> 4) << 14));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    issue_sz(step + 3, sSn);
     issue_a(step + 2, sAn);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int SL = (S + DIST) % 3;                        // slot of step + DIST
@@ -342,9 +411,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
     constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     auto& b0 = bw[S];
     auto& b1 = bw[S1];
-    // Pin the next step's scales as plain register values here, where their loads are
-    // two steps old (left as "-8 * s" the symmetric form sends the register allocator
-    // into heavy spilling; pinned at the load, it would wait for the load at once).
+    // The next step's scales, landed with this step's activations.  Pinned as plain
+    // register values (left as "-8 * s" the symmetric form sends the register allocator
+    // into heavy spilling).
+    if constexpr (SDMA) read_sz(sSb, scl[S1], zsl[S1]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(scl[S1][t]), "+v"(zsl[S1][t]));
 
@@ -420,7 +490,6 @@ void mfma_gemm_kernel(MfmaArgs a) {
     if constexpr (DIST == 3) {
       __builtin_amdgcn_sched_barrier(0);
       load_b(step + DIST, bw[SL]);
-      load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
     }
   };
   // The step count is padded to a multiple of three rather than leaving the unrolled

@@ -147,7 +147,8 @@ def dense_w4a16_sym_f16(m: int = 16, n: int = 512, k: int = 1024, group: int = 1
     rng = _rng(seed)
     x = f32_to_f16_bits(rng.standard_normal((m, k), dtype=np.float32))
     w = random_nibbles_u32(rng, (1, n), k)          # two's complement codes: q uniform in [-8, 7]
-    s = f32_to_f16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
+    ng = 1 if group == 0 else k // group            # group 0: one scale per output channel
+    s = f32_to_f16_bits(rng.uniform(0.005, 0.02, size=(1, n, ng)).astype(np.float32))
     layer = Layer("dense_w4a16_sym_f16", "int4", "f16", "f16", "f16", n, k, group, 1, w, s, None)
     return layer, Acts(x, None, None)
 
@@ -157,8 +158,9 @@ def dense_w4a16_asym_bf16(m: int = 16, n: int = 8192, k: int = 8192, group: int 
     rng = _rng(seed)
     x = f32_to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
     w = random_nibbles_u32(rng, (1, n), k)          # u uniform in [0, 15]
-    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(1, n, k // group)).astype(np.float32))
-    z = rng.integers(6, 10, size=(1, n, k // group), dtype=np.uint8)
+    ng = 1 if group == 0 else k // group            # group 0: one scale per output channel
+    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(1, n, ng)).astype(np.float32))
+    z = rng.integers(6, 10, size=(1, n, ng), dtype=np.uint8)
     layer = Layer("dense_w4a16_asym_bf16", "uint4", "bf16", "bf16", "bf16", n, k, group, 1, w, s, z)
     return layer, Acts(x, None, None)
 

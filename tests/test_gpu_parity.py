@@ -221,6 +221,20 @@ def test_dense_w4a16_sym_f16_mfma_path(m):
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
 
 
+@pytest.mark.parametrize("group,k,m", [(0, 1024, 16), (0, 1024, 300), (0, 4096, 100), (256, 1024, 300),
+                                         (384, 1536, 5), (384, 1536, 300), (384, 3072, 100)])
+def test_dense_scale_group_sizes(group, k, m):
+    # per-channel scales and groups other than 128, including one that is not a power of
+    # two, on the streaming kernel (5, 16 rows), the MFMA kernel and its split-K form
+    # (100 rows: one row tile, two column tiles, K split over workgroups)
+    layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=512, k=k, group=group, seed=20 + group)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+    layer, acts = synth.dense_w4a16_sym_f16(m=m, n=512, k=k, group=group, seed=21 + group)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
 def test_dense_mfma_tile_256_rows():
     # enough row and column tiles for the 256-row tile (and the XCD remap of tile ids)
     layer, acts = synth.dense_w4a16_asym_bf16(m=1536, n=2048, k=512, seed=9)
