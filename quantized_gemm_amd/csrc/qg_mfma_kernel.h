@@ -192,25 +192,32 @@ void mfma_gemm_kernel(MfmaArgs a) {
       }
     }
   };
-  // this lane's scale and z * scale for tile column 32 tt + r, from region reg
-  auto read_sz = [&](const uint8_t* reg, float (&s)[NT], float (&zs)[NT]) {
+  // the 32-bit words holding this lane's stored scale and zero for tile column 32 tt + r,
+  // from region reg (whole words: nothing to extend until the values are used)
+  auto read_sz = [&](const uint8_t* reg, uint32_t (&sb)[NT], uint32_t (&zw)[NT]) {
     if constexpr (SDMA) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const int cl = WCOL * wave + 32 * tt + r, nbl = cl >> 4, c = cl & 15;
-      const uint8_t* sp = reg + 256 * ES * g + 16 * ES * nbl + ES * c;
-      s[tt] = scale_bits_to_f32<ST>(ES == 1 ? (uint32_t)*sp : (uint32_t)*(const uint16_t*)sp);
-      if constexpr (WP == WP_FP4) {
-        zs[tt] = 0.f;
-      } else {
-        float z = 8.0f;
-        if constexpr (ZERO) {
-          const uint32_t zw = *(const uint32_t*)(reg + 1024 + 16 * nbl + 4 * (c >> 3));
-          z = (float)((zw >> ((c & 7) * 4)) & 0xF);
-        }
-        zs[tt] = -z * s[tt];
+      for (int tt = 0; tt < NT; ++tt) {
+        const int cl = WCOL * wave + 32 * tt + r, nbl = cl >> 4, c = cl & 15;
+        sb[tt] = *(const uint32_t*)(reg + 256 * ES * g + 16 * ES * nbl + ((ES * c) & ~3));
+        zw[tt] = ZERO ? *(const uint32_t*)(reg + 1024 + 16 * nbl + 4 * (c >> 3)) : 0u;
       }
     }
+  };
+  // ... and the scale and z * scale they give
+  auto scale_of = [&](const uint32_t (&sb)[NT], const uint32_t (&zw)[NT], float (&s)[NT], float (&zs)[NT]) {
+    if constexpr (SDMA) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const int c = (WCOL * wave + 32 * tt + r) & 15;
+        s[tt] = scale_bits_to_f32<ST>((sb[tt] >> (8 * ((ES * c) & 3))) & (ES == 1 ? 0xFFu : 0xFFFFu));
+        if constexpr (WP == WP_FP4) {
+          zs[tt] = 0.f;
+        } else {
+          const float z = ZERO ? (float)((zw[tt] >> ((c & 7) * 4)) & 0xF) : 8.0f;
+          zs[tt] = -z * s[tt];
+        }
+      }
     }
   };
 
@@ -390,6 +397,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
     uint8_t* const sAb = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
     uint8_t* const sAn = S == 0 ? sA2 : S == 1 ? sA0 : sA1;   // stage of step + 2
     const uint8_t* const sSb = S == 0 ? sS0 : S == 1 ? sS1 : sS2;
+    constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     uint8_t* const sSn = S == 0 ? sS2 : S == 1 ? sS0 : sS1;
     // this wave's A(step) loads have landed; the barrier makes every wave's visible and
     // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
@@ -397,6 +405,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // 16-bit: the first sub-step's activation fragments and the next step's scales are
+    // read before the new loads go out, so that the first MFMAs wait only for them
+    u32x4 Af[MT];   // one fragment register set per row tile (16-bit path)
+    uint32_t sbits[NT], zbits[NT];
+    if constexpr (!F8) {
+      read_a16(sAb, 0, Af);
+      read_sz(sSb, sbits, zbits);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     issue_sz(step + 3, sSn);
     issue_a(step + 2, sAn);
     __builtin_amdgcn_sched_barrier(0);
@@ -408,15 +425,17 @@ void mfma_gemm_kernel(MfmaArgs a) {
       load_scale(min(step + DIST, nsteps - 1), scl[SL], zsl[SL]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     auto& b0 = bw[S];
     auto& b1 = bw[S1];
-    // The next step's scales, landed with this step's activations.  Pinned as plain
-    // register values (left as "-8 * s" the symmetric form sends the register allocator
-    // into heavy spilling).
-    if constexpr (SDMA) read_sz(sSb, scl[S1], zsl[S1]);
+    // The next step's scales are pinned as plain register values (left as "-8 * s" the
+    // symmetric form sends the register allocator into heavy spilling): here for e4m3
+    // (constants), after the first sub-step's MFMAs for the 16-bit paths (their LDS
+    // reads have landed by then).
+    auto pin_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(scl[S1][t]), "+v"(zsl[S1][t]));
+      for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(scl[S1][t]), "+v"(zsl[S1][t]));
+    };
+    if constexpr (F8) pin_scales();
 
     if constexpr (F8) {
       // 2 x MT MFMA pairs per step (k halves j, row tiles mt); each pair's activation
@@ -455,10 +474,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // each row tile come one stage of the next sub-step's dequantization and that tile's
       // next activation fragment read; sched_barrier keeps the order.  Sub-step 3
       // dequantizes sub-step 0 of the next step (its weights and scales are in registers).
-      // one fragment register set per row tile: a tile's next fragment is read into it
-      // right after its MFMAs, one sub-step (MT * NT MFMAs) ahead of use
-      u32x4 Af[MT];
-      read_a16(sAb, 0, Af);
+      // a row tile's next fragment is read into its register set right after its MFMAs,
+      // one sub-step (MT * NT MFMAs) ahead of use
       constexpr int PH = NT * 4;                 // dequant stages per sub-step
       constexpr int PPM = (PH + MT - 1) / MT;    // stages after each row tile
 #pragma unroll
@@ -481,6 +498,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
           if (!last) {
             const int row = 32 * mt + r;
             Af[mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j + 1) ^ ((row >> 1) & 7)));
+          }
+          if (j == 0 && mt == MT - 1) {
+            // the raw words are taken as they are here, so no conversion moves up to
+            // the loads and waits for them there
+#pragma unroll
+            for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(sbits[t]), "+v"(zbits[t]));
+            scale_of(sbits, zbits, scl[S1], zsl[S1]);
+            pin_scales();
           }
           __builtin_amdgcn_sched_barrier(0);
         }
