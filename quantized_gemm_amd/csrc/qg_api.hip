@@ -190,8 +190,8 @@ StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
 constexpr int kCUs = 256;
 constexpr int64_t kStreamMaxRows = 64;
 
-// e4m3 weights and the int4 -> e4m3 path use 128-row tiles only.
-bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8 && pi.wp_mfma != WP_INT4Q_FP8; }
+// The int4 -> e4m3 kernel uses 128-row tiles only.
+bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8; }
 
 // Split K over workgroups when 128-row tiles would fill at most half of the CUs (above
 // that, writing and re-reading the fp32 partials costs more than the idle CUs):

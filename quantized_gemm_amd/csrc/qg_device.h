@@ -204,6 +204,10 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);   // nt: streamed once
 }
+// An empty asm that takes a 32x32 accumulator in VGPRs: the value must be computed
+// before this point (device-only, so that no host pass sees a 512-bit register operand).
+__device__ __forceinline__ void keep_in_vgprs(const f32x16& v) { asm volatile("" ::"v"(v)); }
+
 // 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l (lds is
 // wave-uniform); an out-of-range offset stores zeros.  Kept out of kernel templates: used
 // there directly, the host pass drops the templates' launch stubs.

@@ -28,8 +28,8 @@
 
 namespace qg {
 
-template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int CW, int OCC>
-__global__ __launch_bounds__(64 * CW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int CW>
+__global__ __launch_bounds__(64 * CW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (WP == WP_FP8);
   constexpr int AB = F8 ? 1 : 2;
@@ -466,7 +466,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) { B[t][i] = (int)b0[t][2 * j][i]; B[t][4 + i] = (int)b0[t][2 * j + 1][i]; }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
+        for (int t = 0; t < NT; ++t) {
+          acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
+          // Nothing else depends on an MFMA result, and the code generator otherwise sinks
+          // whole steps of MFMAs below later barriers (no overlap, every fragment live at
+          // once).  The empty asm takes the result here; with the accumulators in VGPRs
+          // (two waves per SIMD) it costs nothing.
+          keep_in_vgprs(acc[mt][t]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -596,16 +603,13 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT = false>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
-  // 16-bit activations: 8 waves (two per SIMD) of BM x 32 for dense tiles and 256-row MoE
-  // blocks; 128-row MoE blocks keep 4 waves of 128 x 64 with two workgroups per CU (their
-  // blocks are many and short, and independent workgroups hide each other's barriers
-  // better: measured 15% faster there, while dense 128-row tiles gain ~10% from 8 waves).
-  // e4m3 weights: 4 waves of 128 x 64, one workgroup per CU.
-  constexpr int CW = (WP != WP_FP8 && (BM == 256 || !MOE)) ? 8 : 4;
-  // two waves per SIMD: one workgroup of 8 waves (256 rows) or two workgroups of 4 (128 rows)
-  static_assert(!(WP == WP_FP8 && BM == 256), "e4m3 weights use 128-row tiles (256 rows spill)");
-  constexpr int OCC = WP == WP_FP8 ? 1 : 2;   // e4m3 wave tiles need > 256 registers
-  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW, OCC>), grid, dim3(64 * CW), 0, st, a);
+  // Two waves per SIMD throughout.  8 waves of BM x 32 for dense tiles, 256-row MoE blocks
+  // and every e4m3 tile; 16-bit 128-row MoE blocks keep 4 waves of 128 x 64 with two
+  // workgroups per CU (their blocks are many and short, and independent workgroups hide
+  // each other's barriers better: measured 15% faster there, while dense 128-row tiles
+  // gain ~10% from 8 waves).
+  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8) ? 8 : 4;
+  hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
@@ -613,8 +617,7 @@ static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, 
   const dim3 grid(t.grid_x, t.grid_y);
   if (moe) {
     if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st); return true; }
-    if constexpr (WP != WP_FP8)
-      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
+    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
   } else {
     if (t.ksplit > 1) {
       if (t.bm != 128) return false;
@@ -622,8 +625,7 @@ static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, 
       return true;
     }
     if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st); return true; }
-    if constexpr (WP != WP_FP8)
-      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
+    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
   }
   return false;
 }

@@ -176,6 +176,20 @@ def dense_w8a8_fp8(m: int = 1, n: int = 7168, k: int = 7168, seed: int = 0):
     return layer, Acts(xq, sx, None)
 
 
+def moe_w8a8_fp8(t: int = 16, experts: int = 8, topk: int = 2, n: int = 256, k: int = 512, seed: int = 0):
+    """MoE W8A8: per-token absmax e4m3 activations, per-(expert, channel) absmax e4m3 weights
+    (N(0, 0.02)), softmax top-k routing of N(0,1) logits."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_rows(rng.standard_normal((t, k), dtype=np.float32))
+    wf = (rng.standard_normal((experts * n, k), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    wq, sw = absmax_e4m3_rows(wf)
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    layer = Layer("moe_w8a8_fp8", "e4m3", "e4m3", "f32", "bf16", n, k, 0, experts,
+                  wq.reshape(experts, n, k), sw.reshape(experts, n, 1), None)
+    return layer, Acts(xq, sx, ids)
+
+
 def moe_w4a16_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096, k: int = 7168,
                     seed: int = 0):
     """MoE W4A16 with MXFP4 weights: e2m1 codes uniform over all 16 codes, UE8M0 exponents 119..123

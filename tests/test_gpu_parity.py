@@ -235,11 +235,17 @@ def test_dense_scale_group_sizes(group, k, m):
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
 
 
-def test_dense_mfma_tile_256_rows():
-    # enough row and column tiles for the 256-row tile (and the XCD remap of tile ids)
-    layer, acts = synth.dense_w4a16_asym_bf16(m=1536, n=2048, k=512, seed=9)
-    y = _run_dense(layer, acts, 1536)
-    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+@pytest.mark.parametrize("kind", ["w4a16", "w8a8"])
+def test_dense_mfma_tile_256_rows(kind):
+    # 25 row tiles (the last one ragged) x 16 column tiles: enough tiles for the 256-row
+    # tile (and the XCD-aware remap of tile ids)
+    m, n, k = 6200, 4096, 256
+    if kind == "w4a16":
+        layer, acts = synth.dense_w4a16_asym_bf16(m=m, n=n, k=k, seed=9)
+    else:
+        layer, acts = synth.dense_w8a8_fp8(m=m, n=n, k=k, seed=9)
+    y = _run_dense(layer, acts, m)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= _tol(layer)
 
 
 @pytest.mark.parametrize("m", [65, 300])
@@ -255,6 +261,15 @@ def test_moe_w4a16_mxfp4_mfma_path(t, experts):
     layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=experts, topk=2, n=320, k=512, seed=11)
     y = _run_moe(layer, acts)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("t,experts", [(5, 8), (40, 8), (400, 4), (1100, 4)])
+def test_moe_w8a8_fp8(t, experts):
+    # e4m3 weights per expert: streaming blocks (10 rows per expert), then MFMA blocks of
+    # 128 (200 rows per expert) and 256 rows (550 rows per expert)
+    layer, acts = synth.moe_w8a8_fp8(t=t, experts=experts, topk=2, n=320, k=512, seed=17)
+    y = _run_moe(layer, acts)
+    assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
 
 
 @pytest.mark.parametrize("m", [8, 100, 300])
