@@ -139,6 +139,9 @@ ALIGN_CASES = [
     ("uniform", 64, 6, 64, 16), ("one_token", 1, 8, 128, 16), ("all_one_expert", 50, 1, 8, 16),
     ("big_block", 300, 8, 128, 64), ("skewed", 1024, 6, 64, 32), ("tiny_block", 33, 3, 5, 1),
     ("many", 8192, 6, 64, 64), ("invalid_ids", 40, 4, 16, 8),
+    # several workgroups, each sorting its own range (2048 ids per workgroup): ragged
+    # ranges with invalid ids near their edges, and the largest expert count
+    ("ragged_invalid", 5001, 5, 100, 16), ("max_experts", 3000, 8, 512, 128),
 ]
 
 
@@ -156,6 +159,10 @@ def test_moe_align_is_bit_exact(case):
     if name == "invalid_ids":
         ids[0, 0] = -1
         ids[5, 2] = experts
+    if name == "ragged_invalid":
+        flat = ids.reshape(-1)
+        for f in (0, 2047, 2048, 4095, 10000, flat.size - 1):
+            flat[f] = -1 if f % 2 else experts + 3
     s, e, n = _align_gpu(ids, experts, bm)
     rs, re_, rn = A.moe_align(ids, experts, bm)
     assert int(n.item()) == rn
