@@ -112,6 +112,16 @@ def topk_from_logits(logits: np.ndarray, topk: int) -> np.ndarray:
     return order[:, :topk].astype(np.int32)
 
 
+def router_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over all experts (float32) taken at the chosen ids, not renormalized: [T, topk].
+
+    The router sits before the hot path; its probabilities are an input of the combine step."""
+    l = np.asarray(logits, dtype=np.float32)
+    e = np.exp(l - np.max(l, axis=1, keepdims=True)).astype(np.float32)
+    p = (e / np.sum(e, axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    return np.take_along_axis(p, np.asarray(ids, dtype=np.int64), axis=1).astype(np.float32)
+
+
 @dataclass
 class Layer:
     """One quantized layer in storage form plus its activations."""
@@ -136,6 +146,7 @@ class Acts:
     x: np.ndarray                  # uint16 bits [M, K] (f16/bf16) or uint8 e4m3 codes [M, K]
     x_scale: np.ndarray | None     # float32 [M] for e4m3 activations
     topk_ids: np.ndarray | None    # int32 [T, topk] for MoE
+    topk_weights: np.ndarray | None = None   # float32 [T, topk]: router probabilities of the chosen experts
 
 
 # ---------------------------------------------------------------------------
@@ -187,7 +198,7 @@ def moe_w8a8_fp8(t: int = 16, experts: int = 8, topk: int = 2, n: int = 256, k: 
     ids = topk_from_logits(logits, topk)
     layer = Layer("moe_w8a8_fp8", "e4m3", "e4m3", "f32", "bf16", n, k, 0, experts,
                   wq.reshape(experts, n, k), sw.reshape(experts, n, 1), None)
-    return layer, Acts(xq, sx, ids)
+    return layer, Acts(xq, sx, ids, router_weights(logits, ids))
 
 
 def moe_w4a16_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096, k: int = 7168,
@@ -201,7 +212,7 @@ def moe_w4a16_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 409
     logits = rng.standard_normal((t, experts), dtype=np.float32)
     ids = topk_from_logits(logits, topk)
     layer = Layer("moe_w4a16_mxfp4", "e2m1", "bf16", "ue8m0", "bf16", n, k, 32, experts, w, s, None)
-    return layer, Acts(x, None, ids)
+    return layer, Acts(x, None, ids, router_weights(logits, ids))
 
 
 def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, k: int = 4096,
@@ -213,7 +224,8 @@ def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, 
     rng = _rng(seed)
     xq, sx = absmax_e4m3_rows(rng.standard_normal((t, k), dtype=np.float32))
     w = random_nibbles_u32(rng, (experts, n), k)    # two's complement codes: q uniform in [-8, 7]
-    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(experts, n, k // group)).astype(np.float32))
+    ng = 1 if group == 0 else k // group            # group 0: one scale per output channel
+    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(experts, n, ng)).astype(np.float32))
     logits = rng.standard_normal((t, experts), dtype=np.float32)
     n_hot = int(round(hot_frac * t))
     hot_tokens = rng.permutation(t)[:n_hot]
@@ -223,7 +235,71 @@ def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, 
     ids = topk_from_logits(logits, topk)
     layer = Layer("moe_w4a8_int4", "int4", "e4m3", "bf16", "bf16", n, k, group, experts, w, s, None,
                   compute="w_to_fp8")
-    return layer, Acts(xq, sx, ids)
+    return layer, Acts(xq, sx, ids, router_weights(logits, ids))
+
+
+# ---------------------------------------------------------------------------
+# The rest of an MoE layer: the down projection's weights and standalone inputs of the
+# steps between and after the two grouped products.  Drawn from their own seeds, so the
+# gate/up workloads above keep their draws.
+# ---------------------------------------------------------------------------
+
+def moe_down_mxfp4(experts: int = 128, n: int = 7168, k: int = 2048, seed: int = 100):
+    """Down projection with MXFP4 weights (K = half the gate/up width): e2m1 codes uniform over all
+    16 codes, UE8M0 exponents 119..123 per 32 elements along K, bf16 activations and output."""
+    rng = _rng(seed)
+    w = rng.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(experts, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    return Layer("moe_down_mxfp4", "e2m1", "bf16", "ue8m0", "bf16", n, k, 32, experts, w, s, None)
+
+
+def moe_down_w4a8(experts: int = 64, n: int = 4096, k: int = 1408, group: int = 128, seed: int = 100):
+    """Down projection of the W4A8 layer: symmetric int4 in [-8, 7], bf16 group scales in
+    [0.005, 0.02], per-row e4m3 activations (the SwiGLU output quantized per row)."""
+    rng = _rng(seed)
+    w = random_nibbles_u32(rng, (experts, n), k)
+    ng = 1 if group == 0 else k // group
+    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(experts, n, ng)).astype(np.float32))
+    return Layer("moe_down_w4a8", "int4", "e4m3", "bf16", "bf16", n, k, group, experts, w, s, None,
+                 compute="w_to_fp8")
+
+
+def gate_up_values(rows: int, inter: int, dtype: str = "bf16", sigma: float = 4.0, seed: int = 0):
+    """Gate/up rows [rows, 2*inter] as f16/bf16 bits: N(0, sigma) values plus a few exact specials
+    (0, +-1, +-20, +-100) in the gate half of the first row (saturation of the sigmoid)."""
+    rng = _rng(seed)
+    v = (rng.standard_normal((rows, 2 * inter), dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    sp = np.array([0.0, 1.0, -1.0, 20.0, -20.0, 100.0, -100.0], dtype=np.float32)
+    if rows > 0:
+        v[0, :min(inter, sp.size)] = sp[:min(inter, sp.size)]
+    return f32_to_bf16_bits(v) if dtype == "bf16" else f32_to_f16_bits(v)
+
+
+def act_rows(rows: int, k: int, dtype: str = "bf16", sigma: float = 4.0, seed: int = 0):
+    """Activation rows of a down product, [rows, k]: N(0, sigma) as f16/bf16 bits, or per-row absmax
+    e4m3 codes + float32 scales (dtype "e4m3")."""
+    rng = _rng(seed)
+    v = (rng.standard_normal((rows, k), dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    if dtype == "e4m3":
+        return absmax_e4m3_rows(v)
+    return (f32_to_bf16_bits(v) if dtype == "bf16" else f32_to_f16_bits(v)), None
+
+
+def slot_outputs(tokens: int, topk: int, n: int, experts: int, dtype: str = "bf16", drop_frac: float = 0.0,
+                 seed: int = 0):
+    """Inputs of the combine step: per-(token, slot) rows [T*topk, N] (f16/bf16 bits, N(0, 4)),
+    router probabilities [T, topk] (softmax of N(0,1) logits at the top-k ids) and the ids, a
+    seeded fraction of slots set to -1 (dropped)."""
+    rng = _rng(seed)
+    y = f32_to_bf16_bits if dtype == "bf16" else f32_to_f16_bits
+    vals = y((rng.standard_normal((tokens * topk, n), dtype=np.float32) * np.float32(4.0)).astype(np.float32))
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    w = router_weights(logits, ids)
+    if drop_frac > 0:
+        drop = rng.random((tokens, topk)) < drop_frac
+        ids = np.where(drop, -1, ids).astype(np.int32)
+    return vals, w, ids
 
 
 WORKLOADS = {
