@@ -32,7 +32,7 @@
  *   buffer of at least that size whose bytes are ZERO before its first use (e.g.
  *   allocated with a zero fill).  Every call leaves it ready for the next call; calls
  *   that share one workspace must not run concurrently (use one per stream).
- * - Shape rules: n % 64 == 0, k % 256 == 0, k % group_k == 0.
+ * - Shape rules: n % 64 == 0, k % 128 == 0, k % group_k == 0.
  */
 #ifndef QG_H_
 #define QG_H_
@@ -75,7 +75,8 @@ enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                 
  * Supported combinations (anything else -> QG_ERR_UNSUPPORTED):
  *   int4 / uint4(+zeros) weights, f16|bf16 scales, group_k a multiple of 128 or 0
  *       (per channel), f16|bf16 activations                          [W4A16]
- *   int4 weights, QG_C_W_TO_FP8, bf16|f16 group-128-multiple scales, e4m3 acts [W4A8]
+ *   int4 weights, QG_C_W_TO_FP8, bf16|f16 scales (group a multiple of 128, or 0 =
+ *       per channel), e4m3 activations                                 [W4A8]
  *   e2m1 weights, UE8M0 scales, group_k == 32, f16|bf16 activations  [MXFP4 W4A16]
  *   e4m3 weights, f32 channel scales (group_k == 0), e4m3 activations [W8A8]
  */
@@ -200,6 +201,51 @@ qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, in
 qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
                       const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
                       int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The rest of an MoE layer.  The pages time an MoE layer as the sum of its gate/up and
+ * down grouped products ("Humming: Fast, Flexible Kernels for Quantized Inference",
+ * benchmark paragraph; "Humming" wiki article, "Reported performance") and do not say
+ * what joins them; this library's reading is the usual SwiGLU feed-forward layer:
+ *
+ *   1. qg_moe_align, then qg_moe_gemm with the gate/up layer (N = 2*I): Y1 [T*topk][2I];
+ *   2. qg_moe_swiglu: act = silu(gate) * up per (token, slot) row -> [T*topk][I];
+ *   3. the down product is qg_moe_gemm itself with the down layer (K = I), called with
+ *      tokens = T*topk and topk = 1 on the SAME align output: flat index f then names input
+ *      row f of act, the sentinel T*topk is unchanged, and Y2[f] = act[f] . W_e^T; its
+ *      block_m is qg_moe_block_m(p_down, T*topk, 1), which must equal the align's block_m
+ *      (it does when both layers use the same kernel family; else align again);
+ *   4. qg_moe_combine: out[t] = sum_j w[t][j] * Y2[t*topk + j] over routed slots.
+ */
+
+/*
+ * qg_moe_swiglu: act[r][i] = silu(g) * u with g = gate_up[r][i], u = gate_up[r][inter + i],
+ * silu(g) = g / (1 + e^-g), computed in float32, for every row r < rows.
+ *   gate_up   device [rows][2*inter], in_type QG_O_F16 or QG_O_BF16 (the gate/up output type)
+ *   out_type  QG_A_F16 / QG_A_BF16: act rounded to nearest even, written to out [rows][inter];
+ *             QG_A_FP8_E4M3: each row quantized for the next product's FP8 activations:
+ *             out_scale[r] = max_i |act[r][i]| / 448 (float32; 1 for an all-zero row) and
+ *             out (uint8 [rows][inter]) = e4m3 codes, round to nearest even of
+ *             clamp(act / out_scale[r], -448, 448)
+ *   out_scale device float32 [rows] for QG_A_FP8_E4M3, else ignored (may be NULL)
+ * inter % 8 == 0 (and inter <= 8192 for QG_A_FP8_E4M3), else QG_ERR_UNSUPPORTED.  Rows of
+ * slots the gate/up product did not write give unspecified values, which nothing reads.
+ */
+qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_t in_type, int32_t out_type,
+                        void* out, float* out_scale, void* stream);
+
+/*
+ * qg_moe_combine: out[t][:] = sum over slots j with 0 <= topk_ids[t][j] < E of
+ * weights[t][j] * y[t*topk + j][:], accumulated in float32 in slot order and rounded once
+ * (nearest even).  Rows of other slots are never read.
+ *   y         device [T*topk][n] of dtype (QG_O_F16 / QG_O_BF16), e.g. the down product's output
+ *   weights   device float32 [T][topk] (the router's probabilities; applied as given)
+ *   topk_ids  device int32 [T][topk]
+ *   out       device [T][n] of dtype, written in full
+ * n % 8 == 0, else QG_ERR_UNSUPPORTED.  Tokens with no routed slot get zeros.
+ */
+qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* topk_ids, int64_t tokens, int32_t topk,
+                         int32_t num_experts, int64_t n, int32_t dtype, void* out, void* stream);
 
 /*
  * qg_dequant: writes expert `expert` of a prepared layer back as dense float32

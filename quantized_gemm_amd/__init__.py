@@ -4,7 +4,8 @@ Argument marshalling only: torch tensors supply device pointers, torch's current
 stream supplies the hipStream_t, and every step of the computation runs in the
 library's HIP kernels.  The entry points mirror include/qg.h one to one:
 ``prepared_bytes``, ``prepare``, ``workspace_bytes``, ``gemm``, ``moe_block_m``,
-``moe_capacity``, ``moe_align``, ``moe_gemm``, ``dequant``, ``status_str``.
+``moe_capacity``, ``moe_align``, ``moe_gemm``, ``moe_swiglu``, ``moe_combine``, ``dequant``,
+``status_str``.
 
 There is no fallback: if libqg.so is missing or cannot be loaded, every call raises.
 """
@@ -26,7 +27,8 @@ C_NATIVE, C_W_TO_FP8 = 0, 1
 STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_ERR_ARCH_MISMATCH",
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
-           "qg_moe_align", "qg_moe_gemm", "qg_dequant", "qg_status_str", "qg_version"]
+           "qg_moe_align", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine", "qg_dequant", "qg_status_str",
+           "qg_version"]
 
 
 class QGError(RuntimeError):
@@ -73,6 +75,9 @@ def lib():
         L.qg_moe_align.restype = i32
         L.qg_moe_gemm.argtypes = [pp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
         L.qg_moe_gemm.restype = i32
+        L.qg_moe_swiglu.argtypes, L.qg_moe_swiglu.restype = [vp, i64, i64, i32, i32, vp, vp, vp], i32
+        L.qg_moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, i32, vp, vp]
+        L.qg_moe_combine.restype = i32
         L.qg_dequant.argtypes, L.qg_dequant.restype = [pp, i32, vp, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
         L.qg_version.argtypes, L.qg_version.restype = [], i32
@@ -162,6 +167,21 @@ def moe_gemm(p: Prepared, x, x_scale, sorted_ids, expert_ids, num_post_pad, toke
     st = lib().qg_moe_gemm(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(sorted_ids), _ptr(expert_ids),
                            _ptr(num_post_pad), tokens, topk, block_m, _ptr(y), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "qg_moe_gemm")
+
+
+def moe_swiglu(gate_up, rows: int, inter: int, in_type: int, out_type: int, out, out_scale=None, stream=None):
+    """act = silu(gate) * up per row (gate = first ``inter`` columns); f16/bf16 or per-row e4m3 output."""
+    st = lib().qg_moe_swiglu(_ptr(gate_up), rows, inter, in_type, out_type, _ptr(out), _ptr(out_scale),
+                             _stream(stream))
+    _check(st, "qg_moe_swiglu")
+
+
+def moe_combine(y, weights, topk_ids, tokens: int, topk: int, num_experts: int, n: int, dtype: int, out,
+                stream=None):
+    """out[t] = sum_j weights[t, j] * y[t*topk + j] over the slots routed inside [0, E)."""
+    st = lib().qg_moe_combine(_ptr(y), _ptr(weights), _ptr(topk_ids), tokens, topk, num_experts, n, dtype, _ptr(out),
+                              _stream(stream))
+    _check(st, "qg_moe_combine")
 
 
 def dequant(p: Prepared, expert: int, out, stream=None):

@@ -84,7 +84,7 @@ qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
   if (d->compute != QG_C_NATIVE && d->compute != QG_C_W_TO_FP8) return QG_ERR_INVALID_ARG;
   if (d->has_zero != 0 && d->has_zero != 1) return QG_ERR_INVALID_ARG;
   if (d->n <= 0 || d->k <= 0 || d->num_experts <= 0 || d->group_k < 0) return QG_ERR_INVALID_ARG;
-  if (d->n % 64 != 0 || d->k % 256 != 0) return QG_ERR_UNSUPPORTED;
+  if (d->n % 64 != 0 || d->k % 128 != 0) return QG_ERR_UNSUPPORTED;
   if (d->n > (1 << 30) || d->k > (1 << 20) || d->num_experts > 4096) return QG_ERR_UNSUPPORTED;
   if (d->group_k != 0 && d->k % d->group_k != 0) return QG_ERR_UNSUPPORTED;
   PathInfo p{};
@@ -537,6 +537,45 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> stream mt=%d grid=%ux%u", (long long)tokens, topk, block_m, t.mt,
          t.grid_x, t.grid_y);
   if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
+qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_t in_type, int32_t out_type, void* out,
+                        float* out_scale, void* stream) {
+  if (rows < 0 || inter <= 0) return QG_ERR_INVALID_ARG;
+  if (in_type != QG_O_F16 && in_type != QG_O_BF16) return QG_ERR_INVALID_ARG;
+  if (out_type != QG_A_F16 && out_type != QG_A_BF16 && out_type != QG_A_FP8_E4M3) return QG_ERR_INVALID_ARG;
+  if (inter % 8 != 0) return QG_ERR_UNSUPPORTED;
+  if (out_type == QG_A_FP8_E4M3 && inter > 8192) return QG_ERR_UNSUPPORTED;
+  if (rows > ((int64_t)1 << 31) - 1 || rows * inter > ((int64_t)1 << 40)) return QG_ERR_UNSUPPORTED;
+  if (rows == 0) return QG_OK;
+  if (!gate_up || !out || !aligned16(gate_up) || !aligned16(out)) return QG_ERR_INVALID_ARG;
+  if (out_type == QG_A_FP8_E4M3 && (!out_scale || ((uintptr_t)out_scale & 3u) != 0)) return QG_ERR_INVALID_ARG;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  const int in_t = in_type == QG_O_F16 ? O_F16 : O_BF16;
+  const int out_t = out_type == QG_A_FP8_E4M3 ? A_FP8 : (out_type == QG_A_F16 ? A_F16 : A_BF16);
+  if (!launch_swiglu(gate_up, rows, inter, in_t, out_t, out, out_type == QG_A_FP8_E4M3 ? out_scale : nullptr,
+                     (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
+qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* topk_ids, int64_t tokens, int32_t topk,
+                         int32_t num_experts, int64_t n, int32_t dtype, void* out, void* stream) {
+  if (tokens < 0 || topk <= 0 || num_experts <= 0 || n <= 0) return QG_ERR_INVALID_ARG;
+  if (dtype != QG_O_F16 && dtype != QG_O_BF16) return QG_ERR_INVALID_ARG;
+  if (n % 8 != 0) return QG_ERR_UNSUPPORTED;
+  if (tokens * topk > ((int64_t)1 << 30) || tokens * n > ((int64_t)1 << 40)) return QG_ERR_UNSUPPORTED;
+  if (tokens == 0) return QG_OK;
+  if (!y || !weights || !topk_ids || !out || !aligned16(y) || !aligned16(out) || ((uintptr_t)weights & 3u) != 0 ||
+      ((uintptr_t)topk_ids & 3u) != 0)
+    return QG_ERR_INVALID_ARG;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  if (!launch_combine(y, weights, topk_ids, tokens, topk, num_experts, n, dtype == QG_O_F16 ? O_F16 : O_BF16, out,
+                      (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();
 }

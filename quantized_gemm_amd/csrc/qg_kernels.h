@@ -71,6 +71,13 @@ struct DequantArgs {
 };
 void launch_dequant(const DequantArgs& a, hipStream_t st);
 
+// MoE layer steps around the grouped products (qg_moe_layer.hip).  in_t / dtype: O_F16 or
+// O_BF16; out_t: A_F16, A_BF16 or A_FP8 (then out_scale receives one scale per row).
+bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, float* out_scale,
+                   hipStream_t st);
+bool launch_combine(const void* y, const float* w, const int32_t* ids, int64_t tokens, int topk, int experts, int64_t n,
+                    int dtype, void* out, hipStream_t st);
+
 void launch_moe_align(const int32_t* ids, int tk, int experts, int block_m, int32_t* sorted_ids, int64_t cap_sorted,
                       int32_t* expert_ids, int64_t cap_blocks, int32_t* num_post_pad, hipStream_t st);
 

@@ -1,5 +1,5 @@
 // MFMA-bound W4A8 GEMM: int4 weights converted to e4m3 in-kernel, e4m3 activations,
-// bf16/f16 group-128 scales.
+// bf16/f16 scales per group of a multiple of 128 along K, or per output channel.
 //
 // "Humming: Fast, Flexible Kernels for Quantized Inference" (device paragraphs) and "Ant
 // Group's Humming ..." (*Coverage reaches beyond standard PTX types*): weights are stored
@@ -7,8 +7,8 @@
 // at larger M the conversion and the scaling are what limits such kernels.  Here:
 //   * int4 -> e4m3 is exact (every value in [-8, 7] is an e4m3 value) and costs a byte
 //     table lookup (v_perm_b32) per 4 weights, once per workgroup tile;
-//   * one 16x16x128 fp8 MFMA covers exactly one 128-wide scale group, so its fp32 result
-//     is promoted into the accumulator with one FMA per output: acc += s[n, g] * P;
+//   * one 16x16x128 fp8 MFMA covers 128 K, which lies inside one scale group, so its fp32
+//     result is promoted into the accumulator with one FMA per output: acc += s[n, g] * P;
 //   * the per-token activation scale is applied in the epilogue.
 // Tile: 128 rows x 256 columns, 4 waves owning 64 columns each; activations staged in
 // LDS (double-buffered, 128-byte row segment per 128-k step, XOR swizzle by row bits
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void mfma_w4a8_kernel(MfmaArgs a) {
   const int64_t col0 = (int64_t)ntile * BN + 64 * wave;
   const int nsteps = a.k >> 7;
   const int64_t kun = a.k >> 5;
-  const int ngroups = a.k / a.group;
+  const int ngroups = a.group == 0 ? 1 : a.k / a.group;   // group 0: one scale per output channel
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)a.w_expert_bytes);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(a.x_rows * a.k));
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void mfma_w4a8_kernel(MfmaArgs a) {
     for (int t = 0; t < NT; ++t) {
       const int64_t nb = wcol[t] >> 4;
       const bool ok = wok[t] && step < nsteps;
-      const int64_t e = (((int64_t)expert * nb_count + nb) * ngroups + step) * 16 + r;
+      const int gi = a.group == 0 ? 0 : (step << 7) / a.group;   // 128-wide step -> scale group
+      const int64_t e = (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + r;
       dst[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, ok ? (int)(e * 2) : kOOB, 0, 0);
     }
   };

@@ -125,3 +125,33 @@ def test_moe_align_rejects_on_the_host():
     assert lib.qg_moe_align(fake, 4, 2, 8, 4, fake, cs, fake, cb - 1, fake, None) == 6
     assert lib.qg_moe_align(fake, 4, 2, 1000, 4, fake, 10 ** 6, fake, 10 ** 6, fake, None) == 2
     assert lib.qg_moe_align(None, 4, 2, 8, 4, fake, cs, fake, cb, fake, None) == 1
+
+
+def test_moe_layer_steps_reject_on_the_host():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    # swiglu: (gate_up, rows, inter, in_type, out_type, out, out_scale, stream)
+    assert lib.qg_moe_swiglu(fake, 0, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 0      # no rows: no-op
+    assert lib.qg_moe_swiglu(fake, -1, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
+    assert lib.qg_moe_swiglu(fake, 4, 0, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
+    assert lib.qg_moe_swiglu(fake, 4, 64, 9, qg.A_BF16, fake, None, None) == 1               # bad input type
+    assert lib.qg_moe_swiglu(fake, 4, 64, qg.O_BF16, 9, fake, None, None) == 1               # bad output type
+    assert lib.qg_moe_swiglu(fake, 4, 60, qg.O_BF16, qg.A_BF16, fake, None, None) == 2       # inter % 8
+    assert lib.qg_moe_swiglu(fake, 4, 8200, qg.O_BF16, qg.A_FP8_E4M3, fake, fake, None) == 2  # e4m3 row too long
+    assert lib.qg_moe_swiglu(None, 4, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
+    assert lib.qg_moe_swiglu(ctypes.c_void_p(4104), 4, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
+    assert lib.qg_moe_swiglu(fake, 4, 64, qg.O_BF16, qg.A_FP8_E4M3, fake, None, None) == 1   # scales missing
+    # combine: (y, weights, ids, tokens, topk, experts, n, dtype, out, stream)
+    assert lib.qg_moe_combine(fake, fake, fake, 0, 2, 8, 64, qg.O_BF16, fake, None) == 0
+    assert lib.qg_moe_combine(fake, fake, fake, 4, 0, 8, 64, qg.O_BF16, fake, None) == 1
+    assert lib.qg_moe_combine(fake, fake, fake, 4, 2, 8, 64, 7, fake, None) == 1
+    assert lib.qg_moe_combine(fake, fake, fake, 4, 2, 8, 60, qg.O_BF16, fake, None) == 2
+    assert lib.qg_moe_combine(fake, None, fake, 4, 2, 8, 64, qg.O_BF16, fake, None) == 1
+    assert lib.qg_moe_combine(fake, ctypes.c_void_p(4098), fake, 4, 2, 8, 64, qg.O_BF16, fake, None) == 1
+
+
+def test_reduction_length_rules():
+    # K must be a multiple of 128 (1408 = 11 * 128 is accepted, 1000 and 1344 are not)
+    assert qg.prepared_bytes(_desc(k=1408)) > 0
+    assert qg.prepared_bytes(_desc(k=1344, group_k=64)) == 0
+    assert qg.prepared_bytes(_desc(k=1344, group_k=0)) == 0
