@@ -127,6 +127,134 @@ def cpu_baseline(builder, wl, budget_cols):
                       f"every M of the sweep {wl['sweep']}"}
 
 
+# The rest of each MoE layer (--layer): the down projection (K = half the gate/up width) and
+# the activation type between the two products.
+LAYERS = {
+    "moe_w4a16_mxfp4": dict(down="moe_down_mxfp4", hidden=7168, inter=2048, act="bf16",
+                            desc="MoE layer MXFP4 W4A16, E=128 top-8, hidden 7168, intermediate 2048: "
+                                 "align + gate/up + SwiGLU + down + combine"),
+    "moe_w4a8_int4": dict(down="moe_down_w4a8", hidden=4096, inter=1408, act="e4m3",
+                          desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: "
+                               "align + gate/up + SwiGLU with per-row e4m3 quantization + down + combine"),
+}
+
+
+def bench_moe_layer(args, wl):
+    """Whole MoE layers: align -> gate/up product -> SwiGLU -> down product (one row per slot)
+    -> routing-weighted combine, each step timed with HIP events on the launch stream."""
+    import torch
+    import quantized_gemm_amd as qg
+    from quantized_gemm_amd import layers, synth
+
+    lw = LAYERS[args.workload]
+    moe = wl["moe"]
+    topk, experts = moe["topk"], moe["experts"]
+    torch.cuda.set_device(0)
+    tmax = max(wl["sweep"])
+    up, acts = getattr(synth, args.workload)(t=tmax, n=wl["n"], k=wl["k"], seed=0, **moe)
+    down = getattr(synth, lw["down"])(experts=experts, n=lw["hidden"], k=lw["inter"], seed=100)
+    pu, bu = layers.prepare_layer(up)
+    pd, bd = layers.prepare_layer(down)
+    copies = args.copies or max(1, int(np.ceil((1 << 30) / (bu.numel() + bd.numel()))))
+    hs = [(pu, pd)]
+    keep = [bu, bd]
+    for _ in range(copies - 1):
+        b1, b2 = bu.clone(), bd.clone()
+        h1, h2 = qg.Prepared.from_buffer_copy(pu), qg.Prepared.from_buffer_copy(pd)
+        h1.dev, h2.dev = b1.data_ptr(), b2.data_ptr()
+        keep += [b1, b2]
+        hs.append((h1, h2))
+    x_all, xs_all = layers.acts_to_dev(acts)
+    ids_all = torch.from_numpy(np.ascontiguousarray(acts.topk_ids)).cuda()
+    w_all = torch.from_numpy(np.ascontiguousarray(acts.topk_weights)).cuda()
+    a_e4m3 = lw["act"] == "e4m3"
+    st = {}
+    for t in wl["sweep"]:
+        rows = t * topk
+        bm = qg.moe_block_m(pu, t, topk)
+        assert qg.moe_block_m(pd, rows, 1) == bm
+        cs, cb = qg.moe_capacity(t, topk, experts, bm)
+        st[t] = dict(
+            bm=bm, sid=torch.empty(cs, dtype=torch.int32, device="cuda"),
+            eid=torch.empty(cb, dtype=torch.int32, device="cuda"), npp=torch.empty(1, dtype=torch.int32, device="cuda"),
+            ids=ids_all[:t].contiguous(), w=w_all[:t].contiguous(),
+            y1=torch.empty((rows, 2 * lw["inter"]), dtype=torch.bfloat16, device="cuda"),
+            act=torch.empty((rows, lw["inter"]), dtype=torch.uint8 if a_e4m3 else torch.bfloat16, device="cuda"),
+            asc=torch.empty(rows, dtype=torch.float32, device="cuda") if a_e4m3 else None,
+            y2=torch.empty((rows, lw["hidden"]), dtype=torch.bfloat16, device="cuda"),
+            out=torch.empty((t, lw["hidden"]), dtype=torch.bfloat16, device="cuda"),
+            ws1=torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda"),
+            ws2=torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda"))
+    stream = torch.cuda.current_stream()
+    names = ["align", "gate_up", "swiglu", "down", "combine"]
+    call = [0]
+
+    def one_step(ev=None):
+        for i, t in enumerate(wl["sweep"]):
+            h1, h2 = hs[call[0] % copies]
+            call[0] += 1
+            d = st[t]
+            rows = t * topk
+            xs = None if xs_all is None else xs_all[:t]
+            mark = (lambda j: ev[i][j].record(stream)) if ev is not None else (lambda j: None)
+            mark(0)
+            qg.moe_align(d["ids"], t, topk, experts, d["bm"], d["sid"], d["eid"], d["npp"])
+            mark(1)
+            qg.moe_gemm(h1, x_all[:t], xs, d["sid"], d["eid"], d["npp"], t, topk, d["bm"], d["y1"], d["ws1"])
+            mark(2)
+            qg.moe_swiglu(d["y1"], rows, lw["inter"], qg.O_BF16, qg.A_FP8_E4M3 if a_e4m3 else qg.A_BF16, d["act"],
+                          d["asc"])
+            mark(3)
+            qg.moe_gemm(h2, d["act"], d["asc"], d["sid"], d["eid"], d["npp"], rows, 1, d["bm"], d["y2"], d["ws2"])
+            mark(4)
+            qg.moe_combine(d["y2"], d["w"], d["ids"], t, topk, experts, lw["hidden"], qg.O_BF16, d["out"])
+            mark(5)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in wl["sweep"]] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s_ in range(args.steps):
+        one_step(ev[s_])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    wb_up, wb_down = weight_bytes(up), weight_bytes(down)
+    per_t, flops_step = {}, 0
+    peak = MFMA_PEAK_TFLOPS[wl["dtype"]]
+    for i, t in enumerate(wl["sweep"]):
+        us = {nm: float(np.mean([ev[s_][i][j].elapsed_time(ev[s_][i][j + 1]) for s_ in range(args.steps)])) * 1e3
+              for j, nm in enumerate(names)}
+        tot = sum(us.values())
+        rows = t * topk
+        f_up = 2 * rows * up.n * up.k
+        f_dn = 2 * rows * down.n * down.k
+        flops_step += f_up + f_dn
+        touched = len(np.unique(acts.topk_ids[:t]))
+        wb = touched * (wb_up + wb_down)
+        per_t[str(t)] = {"us": {k: round(v, 2) for k, v in us.items()}, "layer_us": round(tot, 2),
+                         "gemm_us": round(us["gate_up"] + us["down"], 2),
+                         "tflops_gemms": round((f_up + f_dn) / ((us["gate_up"] + us["down"]) * 1e-6) / 1e12, 2),
+                         "tflops_layer": round((f_up + f_dn) / (tot * 1e-6) / 1e12, 2),
+                         "weight_GBps_gemms": round(wb / ((us["gate_up"] + us["down"]) * 1e-6) / 1e9, 1),
+                         "hbm_frac_gemms": round(wb / ((us["gate_up"] + us["down"]) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "mfma_frac_gemms": round((f_up + f_dn) / ((us["gate_up"] + us["down"]) * 1e-6) / 1e12 / peak, 4),
+                         "touched_experts": touched, "block_m": st[t]["bm"]}
+    result = {
+        "metric": "W4A16 qGEMM TFLOP/s + weight HBM GB/s (% roofline), M=1..4096, dense & MoE",
+        "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"], "data": "synthetic",
+        "config": {"workload": lw["desc"], "t_sweep": wl["sweep"], "weight_copies_rotated": copies,
+                   "weight_bytes_per_expert": {"gate_up": wb_up, "down": wb_down}},
+        "per_t": per_t,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +265,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-cols", type=int, default=8192)
     ap.add_argument("--sweep", type=str, default="", help="comma-separated M values overriding the workload's sweep")
+    ap.add_argument("--layer", action="store_true",
+                    help="MoE workloads: time the whole layer (align, gate/up, SwiGLU, down, combine)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -155,6 +285,12 @@ def main():
     wl = dict(WORKLOADS[args.workload])
     if args.sweep:
         wl["sweep"] = [int(v) for v in args.sweep.split(",")]
+    if args.layer:
+        if args.workload not in LAYERS:
+            print(f"--layer needs an MoE workload ({', '.join(LAYERS)})", file=sys.stderr)
+            sys.exit(2)
+        bench_moe_layer(args, wl)
+        return
     builder = getattr(synth, args.workload)
     torch.cuda.set_device(0)
     mmax = max(wl["sweep"])

@@ -115,3 +115,131 @@ def test_moe_w4a16_mxfp4_e128(t):
 def test_moe_w4a8_int4_e64_skewed(t):
     layer, acts = synth.moe_w4a8_int4(t=t, experts=64, topk=6, n=2816, k=4096, seed=0)
     _moe_check(layer, acts, seed=t)
+
+
+# ---- whole MoE layers at full size ----------------------------------------------------------
+# The layer launches exactly as the benchmark's --layer leg does: tokens are the first T of
+# a draw of the largest T, the gate/up align output feeds both products, the down product
+# runs with one input row per slot.  Sample: a few tokens (first and last included) x the
+# sampled output columns; the oracle computes their gate/up rows in full (SwiGLU needs every
+# column), then the sampled columns of the down product and the weighted sum over slots.
+
+def _layer_gpu(up, down, acts, t, act_type):
+    topk = acts.topk_ids.shape[1]
+    rows, inter = t * topk, down.k
+    pu, bu = layers.prepare_layer(up)
+    pd, bd = layers.prepare_layer(down)
+    bm = qg.moe_block_m(pu, t, topk)
+    assert qg.moe_block_m(pd, rows, 1) == bm
+    cs, cb = qg.moe_capacity(t, topk, up.experts, bm)
+    ids = torch.from_numpy(np.ascontiguousarray(acts.topk_ids[:t], dtype=np.int32)).cuda()
+    sid = torch.empty(cs, dtype=torch.int32, device="cuda")
+    eid = torch.empty(cb, dtype=torch.int32, device="cuda")
+    npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    qg.moe_align(ids, t, topk, up.experts, bm, sid, eid, npp)
+    x, xs = layers.acts_to_dev(acts)
+    x, xs = x[:t], (None if xs is None else xs[:t])
+    y1 = torch.empty((rows, 2 * inter), dtype=torch.bfloat16, device="cuda")
+    ws1 = torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda")
+    qg.moe_gemm(pu, x, xs, sid, eid, npp, t, topk, bm, y1, ws1)
+    e4 = act_type == "e4m3"
+    act = torch.empty((rows, inter), dtype=torch.uint8 if e4 else torch.bfloat16, device="cuda")
+    asc = torch.empty(rows, dtype=torch.float32, device="cuda") if e4 else None
+    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_FP8_E4M3 if e4 else qg.A_BF16, act, asc)
+    y2 = torch.empty((rows, down.n), dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda")
+    qg.moe_gemm(pd, act, asc, sid, eid, npp, rows, 1, bm, y2, ws2)
+    out = torch.full((t, down.n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    w = torch.from_numpy(np.ascontiguousarray(acts.topk_weights[:t])).cuda()
+    qg.moe_combine(y2, w, ids, t, topk, up.experts, down.n, qg.O_BF16, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    return out
+
+
+@pytest.fixture(scope="module")
+def c4_layer():
+    up, acts = synth.moe_w4a16_mxfp4(t=4096, experts=128, topk=8, n=4096, k=7168, seed=0)
+    down = synth.moe_down_mxfp4(experts=128, n=7168, k=2048, seed=100)
+    return up, down, acts
+
+
+@pytest.mark.parametrize("t", [16, 4096])
+def test_moe_layer_mxfp4_e128_full_size(c4_layer, t):
+    from oracle import moe_layer as ML
+    up, down, acts = c4_layer
+    out = _layer_gpu(up, down, acts, t, "bf16")
+    rng = np.random.default_rng(t + 5)
+    toks = np.unique(np.array([0, t - 1, int(rng.integers(0, t))]))
+    cols = _sample(rng, down.n, N_COLS)
+    got = layers.out_bits_to_f64(out[torch.from_numpy(toks).cuda()][:, torch.from_numpy(cols).cuda()])
+    x = R.activations(synth.Acts(acts.x[toks], None, None), "bf16")
+    ref = np.zeros((toks.size, cols.size))
+    for i, tk in enumerate(toks):
+        for j in range(acts.topk_ids.shape[1]):
+            e = int(acts.topk_ids[tk, j])
+            h = R.dense_gemm(x[i:i + 1], R.dequant_layer(up, e))
+            a = ML.swiglu(h)
+            ref[i] += float(acts.topk_weights[tk, j]) * R.dense_gemm(a, R.dequant_rows(down, e, cols))[0]
+    err = R.relative_error(got, ref)
+    assert err <= TOL16, f"T={t}: relative error {err:.3g}"
+
+
+@pytest.mark.parametrize("t", [64, 8192])
+def test_moe_w4a8_layer_steps_full_size(t):
+    # The W4A8 layer's steps at the benchmark's launch shapes, each on generated inputs:
+    # SwiGLU -> e4m3 over T*6 rows of 2*1408, the down product (E=64, N=4096, K=1408, slot
+    # rows, with the widening workspace) and the combine over N=4096.
+    from oracle import moe_layer as ML
+    from oracle import formats as F
+    topk, inter, hidden = 6, 1408, 4096
+    _, acts = synth.moe_w4a8_int4(t=t, experts=64, topk=topk, n=64, k=256, seed=0)
+    rows = t * topk
+    rng = np.random.default_rng(t)
+    # SwiGLU -> e4m3
+    gu = synth.gate_up_values(rows, inter, "bf16", seed=t)
+    codes = torch.empty((rows, inter), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    qg.moe_swiglu(torch.from_numpy(gu.view(np.int16)).cuda(), rows, inter, qg.O_BF16, qg.A_FP8_E4M3, codes, sc)
+    torch.cuda.synchronize()
+    rr = _sample(rng, rows, N_ROWS)
+    act, rc, rs = ML.swiglu_e4m3(F.decode_act(gu[rr], "bf16"))
+    c_gpu, s_gpu = codes.cpu().numpy()[rr], sc.cpu().numpy()[rr]
+    np.testing.assert_allclose(s_gpu, rs, rtol=2.0 ** -20)
+    assert np.mean(c_gpu == rc) >= 0.99
+    assert R.relative_error(F.decode_e4m3(c_gpu) * s_gpu[:, None].astype(np.float64), act) <= 2.0 ** -4
+    # down product on generated e4m3 rows
+    down = synth.moe_down_w4a8(experts=64, n=hidden, k=inter, seed=100)
+    pd, bd = layers.prepare_layer(down)
+    bm = qg.moe_block_m(pd, rows, 1)
+    cs, cb = qg.moe_capacity(t, topk, 64, bm)
+    ids = torch.from_numpy(np.ascontiguousarray(acts.topk_ids, dtype=np.int32)).cuda()
+    sid = torch.empty(cs, dtype=torch.int32, device="cuda")
+    eid = torch.empty(cb, dtype=torch.int32, device="cuda")
+    npp = torch.empty(1, dtype=torch.int32, device="cuda")
+    qg.moe_align(ids, t, topk, 64, bm, sid, eid, npp)
+    xq, xs = synth.act_rows(rows, inter, "e4m3", seed=t + 1)
+    y2 = torch.full((rows, hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda")
+    qg.moe_gemm(pd, torch.from_numpy(xq).cuda(), torch.from_numpy(xs).cuda(), sid, eid, npp, rows, 1, bm, y2, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y2).all())
+    slots, cols = _sample(rng, rows, N_ROWS), _sample(rng, hidden, N_COLS)
+    got = layers.out_bits_to_f64(y2[torch.from_numpy(slots).cuda()][:, torch.from_numpy(cols).cuda()])
+    ref = np.empty_like(got)
+    for i, sl in enumerate(slots):
+        e = int(acts.topk_ids[sl // topk, sl % topk])
+        a = F.decode_e4m3(xq[sl:sl + 1]) * float(xs[sl])
+        ref[i] = R.dense_gemm(a, R.dequant_rows(down, e, cols))[0]
+    assert R.relative_error(got, ref) <= TOL8
+    # combine over N = 4096 on generated slot rows and router probabilities
+    yv, w, cids = synth.slot_outputs(t, topk, hidden, experts=64, seed=t + 2)
+    out = torch.empty((t, hidden), dtype=torch.bfloat16, device="cuda")
+    qg.moe_combine(torch.from_numpy(yv.view(np.int16)).cuda(), torch.from_numpy(w).cuda(),
+                   torch.from_numpy(cids).cuda(), t, topk, 64, hidden, qg.O_BF16, out)
+    torch.cuda.synchronize()
+    toks = _sample(rng, t, 8)
+    yh = F.decode_act(yv.reshape(t, topk, hidden)[toks], "bf16")
+    refc = ML.combine(yh, w[toks], cids[toks], 64)
+    gotc = layers.out_bits_to_f64(out[torch.from_numpy(toks).cuda()])
+    assert R.relative_error(gotc, refc) <= 2.0 ** -8 + 2.0 ** -16
