@@ -372,14 +372,37 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    # Per-launch durations: each M alone, `steps` back-to-back launches (rotating weight
+    # copies) between two events on the launch stream, so that one event pair's overhead is
+    # spread over many launches (the figure rocprof's kernel trace gives as the average
+    # duration).  The single-launch event pairs of the timed steps are reported beside it.
+    batch = {}
+    for m in wl["sweep"]:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        xs = None if xs_all is None else xs_all[:m]
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            h = handles[call[0] % copies]
+            call[0] += 1
+            if moe:
+                bm, sid, eid, npp, ids = align[m]
+                qg.moe_gemm(h, x_all[:m], xs, sid, eid, npp, m, moe["topk"], bm, ys[m], ws[m])
+            else:
+                qg.gemm(h, x_all[:m], xs, ys[m], m, ws[m])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        batch[m] = e0.elapsed_time(e1) * 1e-3 / args.steps
+
     flops_step = sum(2 * rows_of[m] * layer.n * layer.k for m in wl["sweep"])
     per_m = {}
     for i, m in enumerate(wl["sweep"]):
         d = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]) * 1e-3
-        avg = float(d.mean())
+        avg = batch[m]
         fl = 2 * rows_of[m] * layer.n * layer.k
         wb = wbytes_of[m]
-        per_m[str(m)] = {"us": round(avg * 1e6, 2), "us_median": round(float(np.median(d)) * 1e6, 2),
+        per_m[str(m)] = {"us": round(avg * 1e6, 2), "us_single_launch": round(float(d.mean()) * 1e6, 2),
+                         "us_single_median": round(float(np.median(d)) * 1e6, 2),
                          "tflops": round(fl / avg / 1e12, 2), "weight_GBps": round(wb / avg / 1e9, 1),
                          "hbm_frac": round(wb / avg / 1e9 / HBM_PEAK_GBPS, 4),
                          "mfma_frac": round(fl / avg / 1e12 / MFMA_PEAK_TFLOPS[wl["dtype"]], 4)}
