@@ -215,6 +215,31 @@ def moe_w4a16_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 409
     return layer, Acts(x, None, ids, router_weights(logits, ids))
 
 
+def dense_w4a8_mxfp4(m: int = 16, n: int = 4096, k: int = 7168, out: str = "bf16", seed: int = 0):
+    """Dense W4A8 with MXFP4 weights: e2m1 codes uniform over all 16 codes, UE8M0 exponents 119..123
+    per 32 elements along K, per-token absmax e4m3 activations of N(0,1) rows."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_rows(rng.standard_normal((m, k), dtype=np.float32))
+    w = rng.integers(0, 256, size=(1, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(1, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    layer = Layer("dense_w4a8_mxfp4", "e2m1", "e4m3", "ue8m0", out, n, k, 32, 1, w, s, None)
+    return layer, Acts(xq, sx, None)
+
+
+def moe_w4a8_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096, k: int = 7168, seed: int = 0):
+    """MoE W4A8 with MXFP4 weights (the MXFP4 workload's weights and routing with per-token absmax e4m3
+    activations instead of bf16): e2m1 codes uniform, UE8M0 exponents 119..123 per 32 along K, softmax
+    top-k routing of N(0,1) logits."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_rows(rng.standard_normal((t, k), dtype=np.float32))
+    w = rng.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(experts, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    layer = Layer("moe_w4a8_mxfp4", "e2m1", "e4m3", "ue8m0", "bf16", n, k, 32, experts, w, s, None)
+    return layer, Acts(xq, sx, ids, router_weights(logits, ids))
+
+
 def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, k: int = 4096,
                   group: int = 128, hot_frac: float = 0.2, hot_experts=(0, 1, 2, 3), hot_bias: float = 3.0,
                   seed: int = 0):
@@ -264,6 +289,14 @@ def moe_down_w4a8(experts: int = 64, n: int = 4096, k: int = 1408, group: int = 
                  compute="w_to_fp8")
 
 
+def moe_down_w4a8_mxfp4(experts: int = 128, n: int = 7168, k: int = 2048, seed: int = 100):
+    """Down projection of the W4A8 MXFP4 layer: MXFP4 weights drawn like moe_down_mxfp4, e4m3
+    activations (the SwiGLU output quantized per row)."""
+    layer = moe_down_mxfp4(experts=experts, n=n, k=k, seed=seed)
+    layer.name, layer.a_type = "moe_down_w4a8_mxfp4", "e4m3"
+    return layer
+
+
 def gate_up_values(rows: int, inter: int, dtype: str = "bf16", sigma: float = 4.0, seed: int = 0):
     """Gate/up rows [rows, 2*inter] as f16/bf16 bits: N(0, sigma) values plus a few exact specials
     (0, +-1, +-20, +-100) in the gate half of the first row (saturation of the sigmoid)."""
@@ -308,4 +341,6 @@ WORKLOADS = {
     "dense_w8a8_fp8": dense_w8a8_fp8,
     "moe_w4a16_mxfp4": moe_w4a16_mxfp4,
     "moe_w4a8_int4": moe_w4a8_int4,
+    "dense_w4a8_mxfp4": dense_w4a8_mxfp4,
+    "moe_w4a8_mxfp4": moe_w4a8_mxfp4,
 }

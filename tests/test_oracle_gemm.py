@@ -199,3 +199,32 @@ def test_moe_w4a8_matches_explicit_scale_factorisation():
         ref = np.array([sum(float(acts.x_scale[t]) * np.dot(xv[g*128:(g+1)*128], q[n_, g*128:(g+1)*128]) * s[n_, g]
                             for g in range(2)) for n_ in range(16)])
         assert np.allclose(y[t, 0], ref, rtol=1e-13, atol=1e-13)
+
+
+# ---- e2m1 weights x e4m3 activations (W4A8 MXFP4) ----------------------------------------
+
+def test_w4a8_mxfp4_brute_force_is_exact():
+    # every product e2m1 * 2^(E-127) * e4m3 * 2^j is exact in float64, and so is the sum of a
+    # few of them: the vectorised oracle must equal per-element decoding and triple loops
+    layer, acts = synth.dense_w4a8_mxfp4(m=3, n=16, k=64, seed=4)
+    acts.x_scale = np.array([0.5, 2.0, 0.25], np.float32)          # powers of two: exact
+    y = R.dense_reference(layer, acts)
+    nib = F.unpack_u8_nibbles(layer.w[0])
+    e8 = layer.s[0].astype(np.int64)
+    ref = np.zeros((3, 16))
+    for m in range(3):
+        for n in range(16):
+            for k in range(64):
+                w = float(F.decode_e2m1(nib[n, k])) * 2.0 ** (int(e8[n, k // 32]) - 127)
+                ref[m, n] += float(F.decode_e4m3(acts.x[m, k])) * float(acts.x_scale[m]) * w
+    assert np.array_equal(y, ref)
+
+
+def test_w4a8_mxfp4_reduces_to_w4a16_mxfp4_on_the_same_values():
+    # every e4m3 value is a bf16 value: with scale 1 the same activations written as bf16 give
+    # exactly the same oracle product
+    layer, acts = synth.dense_w4a8_mxfp4(m=4, n=32, k=256, seed=5)
+    acts.x_scale = np.ones(4, np.float32)
+    x16 = synth.f32_to_bf16_bits(F.decode_e4m3(acts.x).astype(np.float32))
+    l16 = synth.Layer("t", "e2m1", "bf16", "ue8m0", "bf16", 32, 256, 32, 1, layer.w, layer.s, None)
+    assert np.array_equal(R.dense_reference(layer, acts), R.dense_reference(l16, synth.Acts(x16, None, None)))
