@@ -112,10 +112,15 @@ qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
     }
     p.st = d->s_type == QG_S_F16 ? S_F16 : S_BF16;
   } else if (d->w_type == QG_W_FP4_E2M1) {
-    if (!act16 || d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 32 || d->s_type != QG_S_UE8M0)
+    if (d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 32 || d->s_type != QG_S_UE8M0)
       return QG_ERR_UNSUPPORTED;
-    if (d->out_type != (d->a_type == QG_A_F16 ? QG_O_F16 : QG_O_BF16)) return QG_ERR_UNSUPPORTED;
-    p.wp_small = WP_FP4; p.order = 0; p.w4 = 1; p.af = d->a_type == QG_A_F16 ? A_F16 : A_BF16; p.st = S_UE8M0;
+    if (act16) {
+      if (d->out_type != (d->a_type == QG_A_F16 ? QG_O_F16 : QG_O_BF16)) return QG_ERR_UNSUPPORTED;
+      p.af = d->a_type == QG_A_F16 ? A_F16 : A_BF16;
+    } else {
+      p.af = A_FP8;   // W4A8 MXFP4: e2m1 codes and UE8M0 scales are operands of the scaled fp8/fp4 MFMA
+    }
+    p.wp_small = WP_FP4; p.order = 0; p.w4 = 1; p.st = S_UE8M0;
     p.dq_wp = WP_FP4;
   } else {  // e4m3
     if (d->a_type != QG_A_FP8_E4M3 || d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 0 ||
@@ -201,7 +206,7 @@ bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8; }
 constexpr int kMaxSplit = 8;
 int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
   if (pi.wp_mfma == WP_INT4Q_FP8 || tiles * 2 > kCUs) return 1;
-  const int64_t bk = pi.wp_mfma == WP_FP8 ? 128 : 64;
+  const int64_t bk = pi.af == A_FP8 ? 128 : 64;   // K per step: fp8 MFMAs take 128
   const int64_t steps = k / bk;
   int sp = 1;
   while (sp < kMaxSplit && tiles * sp * 2 <= kCUs && steps % (sp * 2) == 0 && steps / (sp * 2) >= 8 &&
@@ -226,7 +231,7 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   static const char* ks = getenv("QG_KSPLIT");
   if (ks && t.bm == 128 && pi.wp_mfma != WP_INT4Q_FP8) {
     const int v = atoi(ks);
-    const int64_t bk = pi.wp_mfma == WP_FP8 ? 128 : 64;
+    const int64_t bk = pi.af == A_FP8 ? 128 : 64;
     if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / bk) % v == 0 && (group <= 0 || (k / v) % group == 0))
       t.ksplit = v;
   }
@@ -596,7 +601,8 @@ qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* str
   a.n = (int)p->desc.n; a.k = (int)p->desc.k;
   a.groups = p->desc.group_k == 0 ? 1 : (int)(p->desc.k / p->desc.group_k);
   a.group = p->desc.group_k;
-  a.wp = pi.dq_wp; a.af = pi.af; a.stype = pi.st; a.zero = p->desc.has_zero;
+  a.wp = pi.dq_wp; a.af = pi.dq_wp == WP_FP4 && pi.af == A_FP8 ? A_BF16 : pi.af;   // e2m1 reads back through bf16
+  a.stype = pi.st; a.zero = p->desc.has_zero;
   launch_dequant(a, (hipStream_t)stream);
   return launched();
 }

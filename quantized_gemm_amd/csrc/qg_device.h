@@ -179,6 +179,13 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// e4m3 activations x e2m1 weights (format code 4) with the weights' UE8M0 block scale:
+// each lane passes the biased exponent of the 32 K it holds of its column (sb); the
+// activation operand's scale is neutral.  The e2m1 operand uses the low 4 dwords of b.
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8_fp4(i32x8 a, i32x8 b, int sb, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
+}
+
 template <int AF>
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (AF == A_F16)
@@ -188,6 +195,9 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8_fp4(i32x8 a, i32x8 b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
 }
 
 // ---- loads -------------------------------------------------------------------------

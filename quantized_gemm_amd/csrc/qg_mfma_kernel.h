@@ -8,7 +8,9 @@
 //     with z*s precomputed, rounded once to bf16/f16;
 //   * e2m1: hardware e2m1 -> bf16/f16 conversion with the UE8M0 scale folded in;
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
-//     in the epilogue.
+//     in the epilogue;
+//   * e4m3 x e2m1 (W4A8 MXFP4): no dequantization at all, the e2m1 codes and their UE8M0
+//     block scales are operands of the scaled fp8/fp4 MFMA; per-token scale in the epilogue.
 //
 // Tile: BM x 256 per workgroup, CW waves, wave w owning all BM rows of the columns
 // [w 256/CW, (w+1) 256/CW), so that every weight is dequantized exactly once per tile.
@@ -31,7 +33,8 @@ namespace qg {
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int CW>
 __global__ __launch_bounds__(64 * CW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mfma_gemm_kernel(MfmaArgs a) {
-  constexpr bool F8 = (WP == WP_FP8);
+  constexpr bool F8 = (AF == A_FP8);                 // e4m3 activations: fp8 MFMAs
+  constexpr bool FP4B = F8 && WP == WP_FP4;           // ... with e2m1 weights as the second operand
   constexpr int AB = F8 ? 1 : 2;
   constexpr int BK = F8 ? 128 : 64;          // K per step; one LDS row segment = 128 bytes
   constexpr int NTHR = 64 * CW;              // CW waves, each owning BN / CW columns and all BM rows
@@ -43,7 +46,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int STAGE = BM * ROWB;
   constexpr int NS = 3;                      // activation stages in LDS (ring)
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
-  constexpr int BU = F8 ? 4 : 1;             // 16-byte weight units per lane per tile and step
+  constexpr int BU = F8 ? (FP4B ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step
   // elements held by the bytes of the low / high nibble words of a 4-bit code word
   constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
   constexpr int M0[4] = {0, QUAD ? 1 : 4, QUAD ? 2 : 1, QUAD ? 3 : 5};
@@ -90,7 +93,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
     const int mtiles = (int)((a.m + BM - 1) / BM);
     const int ntiles = (int)gridDim.x / mtiles;
     const int id = blockIdx.x;
-    const int64_t rowb = (int64_t)a.k * AB, colb = F8 ? a.k : a.k / 2;   // bytes per row / column
+    const int64_t rowb = (int64_t)a.k * AB, colb = WP == WP_FP8 ? a.k : a.k / 2;   // bytes per row / column
     int xr = 0;
     int64_t best = 0;
     for (int cand = 1; cand <= 8; cand <<= 1) {
@@ -133,7 +136,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // sums (the host makes the slices whole scale groups); otherwise all of K.
   const int nsteps = SPLIT ? a.k / BK / a.ksplit : a.k / BK;
   const int kstep0 = SPLIT ? (int)blockIdx.z * nsteps : 0;
-  const int64_t kun = F8 ? (a.k >> 4) : (a.k >> 5);
+  const int64_t kun = WP == WP_FP8 ? (a.k >> 4) : (a.k >> 5);   // 16-byte units along K per column
   const int ngroups = a.group == 0 ? 1 : a.k / a.group;
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)a.w_expert_bytes);
@@ -237,9 +240,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
       const int64_t nb = wcol[t] >> 4, c = wcol[t] & 15;
 #pragma unroll
       for (int u = 0; u < BU; ++u) {
-        // 4-bit: unit (step*2 + g) covers k = 64*step + 32g ..; fp8: units 8*step + 4g + u
+        // 4-bit: unit (step*2 + g) covers k = 64*step + 32g ..; fp8: units 8*step + 4g + u;
+        // e2m1 under e4m3 activations: unit 4*step + 2u + g covers k = 128*step + 64u + 32g ..,
+        // the e2m1 operand of MFMA u on this lane
         const int64_t gs = (int64_t)(kstep0 + step);
-        const int64_t ku = F8 ? (gs * 8 + 4 * g + u) : (gs * 2 + g);
+        const int64_t ku = F8 ? (FP4B ? gs * 4 + 2 * u + g : gs * 8 + 4 * g + u) : (gs * 2 + g);
         const bool ok = wok[t] && step < nsteps;
         // cached: every weight tile is read again by the other row tiles of the XCD
         dst[t][u] = bload16(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
@@ -251,7 +256,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t nb = min((int64_t)nb_count - 1, wcol[t] >> 4), c = wcol[t] & 15;
-      if constexpr (WP == WP_FP4) {
+      if constexpr (FP4B) {
+        // the UE8M0 exponents of the lane's two units (groups 4*step + 2u + g), bytes 0 and 1
+        // of one word kept in the float slot as raw bits; the MFMA applies them
+        const uint8_t* sp = (const uint8_t*)a.s + (((int64_t)expert * nb_count + nb) * ngroups +
+                                                   (int64_t)(kstep0 + step) * 4 + g) * 16 + c;
+        s[t] = __uint_as_float((uint32_t)sp[0] | ((uint32_t)sp[32] << 8));
+        zs[t] = 0.f;
+      } else if constexpr (WP == WP_FP4) {
         const int64_t gi = (int64_t)(kstep0 + step) * 2 + g;   // group 32 == unit
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         zs[t] = 0.f;
@@ -446,9 +458,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
       auto read_a8 = [&](int q) -> i32x8 {
         const int j = q / MT, mt = q % MT;
         const int row = 32 * mt + r;
-        const int lc0 = 4 * g + 2 * j;
+        // The fp8 operand of lane g holds k = 16g .. 16g+15 of the MFMA's 64 in its first 16
+        // bytes and k = 32 + 16g .. in the other 16.  With e4m3 weights both operands take
+        // any common order (here 32 contiguous bytes per lane); the e2m1 operand's order is
+        // fixed (k = 32g + i), so then the activations follow it: MFMA j covers k = 64j ..
+        const int lc0 = FP4B ? 4 * j + g : 4 * g + 2 * j;
+        const int lc1 = FP4B ? lc0 + 2 : lc0 + 1;
         const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
-        const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
+        const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc1 ^ ((row >> 1) & 7)));
         i32x8 A;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
@@ -466,10 +483,17 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { B[t][i] = (int)b0[t][2 * j][i]; B[t][4 + i] = (int)b0[t][2 * j + 1][i]; }
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (FP4B) { B[t][i] = (int)b0[t][j][i]; B[t][4 + i] = 0; }
+            else { B[t][i] = (int)b0[t][2 * j][i]; B[t][4 + i] = (int)b0[t][2 * j + 1][i]; }
+          }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
+          if constexpr (FP4B)
+            acc[mt][t] = mfma32x32x64_fp8_fp4(Af8[q % 3], B[t], (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu),
+                                              acc[mt][t]);
+          else
+            acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
           // Nothing else depends on an MFMA result, and the code generator otherwise sinks
           // whole steps of MFMAs below later barriers (no overlap, every fragment live at
           // once).  The empty asm takes the result here; with the accumulators in VGPRs
@@ -563,7 +587,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   const int64_t col0w = col0;                        // first column of this wave
   float sw[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) sw[t] = F8 && !SPLIT ? ((const float*)a.s)[(int64_t)expert * a.n + wcol[t]] : 1.f;
+  for (int t = 0; t < NT; ++t) sw[t] = WP == WP_FP8 && !SPLIT ? ((const float*)a.s)[(int64_t)expert * a.n + wcol[t]] : 1.f;
   constexpr int HALVES = 32 / CR;                    // chunks per 32-row tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -617,7 +641,7 @@ static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // workgroups per CU (their blocks are many and short, and independent workgroups hide
   // each other's barriers better: measured 15% faster there, while dense 128-row tiles
   // gain ~10% from 8 waves).
-  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8) ? 8 : 4;
+  constexpr int CW = (BM == 256 || !MOE || AF == A_FP8) ? 8 : 4;
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 

@@ -17,6 +17,8 @@
 //  * e2m1 x 16-bit: the UE8M0 block scale is folded into the hardware e2m1 -> bf16/f16
 //    conversion (exact).
 //  * e4m3 x e4m3: fp8 MFMA, per-token x per-channel scale in the epilogue.
+//  * e4m3 x e2m1 (W4A8 MXFP4): the e2m1 codes and their UE8M0 block scales go to the
+//    scaled fp8/fp4 MFMA as they are; per-token scale in the epilogue.
 //
 // Work split inside a workgroup of NCB x KQ waves: wave (cb, q) owns 16-column block cb
 // and the q-th contiguous part of K.  Activations, scales and zero points for all parts
@@ -255,6 +257,25 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                   B[i] = (int)bw[c][0][i]; B[4 + i] = (int)bw[c][1][i];
                 }
                 acc[mt] = mfma16x16x128_fp8(A, B, acc[mt]);
+              }
+            } else if constexpr (WP == WP_FP4 && AF == A_FP8) {
+              // e4m3 activations x e2m1 weights, natively: the lane's 16-byte unit is the
+              // e2m1 operand of one 16x16x128 scaled MFMA (k = 32g + i at nibble i, low nibble
+              // first), and the UE8M0 exponent of those 32 K (group 4*chunk + g) is its block
+              // scale.  The e4m3 operand of lane g holds k = 16g .. 16g+15 in its first 16
+              // bytes and k = 64 + 16g .. in the other 16 (the fp8 operand's K order).
+              const int e8 = sS[slot * 64 + g * 16 + r];
+              i32x8 B;
+    #pragma unroll
+              for (int i = 0; i < 4; ++i) { B[i] = (int)bw[c][0][i]; B[4 + i] = 0; }
+    #pragma unroll
+              for (int mt = 0; mt < NMT; ++mt) {
+                const uint8_t* ap = arow0 + (16 * mt + ar) * AROW + 16 * g;
+                const u32x4 a0 = *(const u32x4*)ap, a1 = *(const u32x4*)(ap + 64);
+                i32x8 A;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) { A[i] = aok ? (int)a0[i] : 0; A[4 + i] = aok ? (int)a1[i] : 0; }
+                acc[mt] = mfma16x16x128_fp8_fp4(A, B, e8, acc[mt]);
               }
             } else if constexpr (WP == WP_FP4) {
               // group 32 == one 16-byte unit: the lane's scale is group 4*chunk + g
