@@ -48,6 +48,12 @@ WORKLOADS = {
     "moe_w4a16_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="bf16", moe=dict(experts=128, topk=8),
                             desc="MoE W4A16 MXFP4 (e2m1 + UE8M0/32), E=128 top-8, fused gate+up N=4096, K=7168, "
                                  "bf16 activations; T sweep"),
+    "dense_w4a8_mxfp4": dict(sweep=[1, 16, 128, 1024, 4096], n=8192, k=8192, dtype="fp8",
+                             desc="dense W4A8 MXFP4 (e2m1 + UE8M0/32 weights x per-token e4m3 activations, scaled "
+                                  "fp8 x fp4 MFMAs), N=K=8192; M sweep"),
+    "moe_w4a8_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="fp8", moe=dict(experts=128, topk=8),
+                           desc="MoE W4A8 MXFP4 (e2m1 + UE8M0/32 x per-token e4m3, scaled fp8 x fp4 MFMAs), E=128 "
+                                "top-8, fused gate+up N=4096, K=7168; T sweep"),
     "moe_w4a8_int4": dict(sweep=[64, 1024, 8192], n=2816, k=4096, dtype="bf16", moe=dict(experts=64, topk=6),
                           desc="MoE W4A8 int4 weights with bf16 group-128 scales x per-token e4m3 activations, "
                                "E=64 top-6, N=2816, K=4096, 20% of tokens biased to 4 hot experts; T sweep"),
@@ -133,6 +139,9 @@ LAYERS = {
     "moe_w4a16_mxfp4": dict(down="moe_down_mxfp4", hidden=7168, inter=2048, act="bf16",
                             desc="MoE layer MXFP4 W4A16, E=128 top-8, hidden 7168, intermediate 2048: "
                                  "align + gate/up + SwiGLU + down + combine"),
+    "moe_w4a8_mxfp4": dict(down="moe_down_w4a8_mxfp4", hidden=7168, inter=2048, act="e4m3",
+                           desc="MoE layer W4A8 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: align + gate/up + "
+                                "SwiGLU with per-row e4m3 quantization + down + combine"),
     "moe_w4a8_int4": dict(down="moe_down_w4a8", hidden=4096, inter=1408, act="e4m3",
                           desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: "
                                "align + gate/up + SwiGLU with per-row e4m3 quantization + down + combine"),
