@@ -70,3 +70,56 @@ def moe_align_bruteforce(topk_ids, experts: int, block_m: int):
             expert_ids[pos // block_m + b] = e
         pos += nblk * block_m
     return np.array(sorted_ids, np.int32), np.array(expert_ids, np.int32), pos
+
+
+# ---------------------------------------------------------------------------------------
+# Grouped MoE input organizations ("Humming" wiki article, "Device and workload selection":
+# grouped-contiguous execution keeps each expert's rows together; grouped-masked execution
+# gives each expert its own storage with a count of valid rows).  Both name input rows
+# directly, so their block map is the contract above applied to one expert id per row
+# (topk = 1, flat index = row index):
+#   contiguous: rows [offsets[e], offsets[e+1]) belong to expert e; rows_total = offsets[E];
+#   masked:     row e*cap + i belongs to expert e for i < counts[e] (counts clamped to
+#               [0, cap]); the other rows of the storage are not used; rows_total = E*cap.
+# The sentinel is rows_total.
+
+def grouped_row_experts(layout: str, arr, experts: int, cap: int = 0) -> np.ndarray:
+    """Expert id of every input row (-1: unused row), int64 [rows_total]."""
+    a = np.asarray(arr, dtype=np.int64)
+    if layout == "contiguous":
+        assert a.size == experts + 1 and a[0] == 0 and np.all(np.diff(a) >= 0)
+        return np.repeat(np.arange(experts), np.diff(a))
+    assert layout == "masked" and a.size == experts
+    cnt = np.clip(a, 0, cap)
+    i = np.arange(cap)[None, :]
+    return np.where(i < cnt[:, None], np.arange(experts)[:, None], -1).reshape(-1)
+
+
+def grouped_map(layout: str, arr, experts: int, block_m: int, cap: int = 0):
+    """(sorted_ids, expert_ids, num_post_pad) of a grouped organization, with the indexed path's
+    capacity for rows_total rows and topk = 1."""
+    ids = grouped_row_experts(layout, arr, experts, cap)
+    return moe_align(ids.reshape(-1, 1), experts, block_m)
+
+
+def grouped_map_direct(layout: str, arr, experts: int, block_m: int, cap: int = 0):
+    """The same map written out expert by expert with loops, for pinning grouped_map."""
+    a = [int(v) for v in np.asarray(arr).reshape(-1)]
+    total = a[experts] if layout == "contiguous" else experts * cap
+    cs, cb = capacity(total, 1, experts, block_m)
+    sorted_ids = [total] * cs
+    expert_ids = [-1] * cb
+    pos = 0
+    for e in range(experts):
+        if layout == "contiguous":
+            rows = list(range(a[e], a[e + 1]))
+        else:
+            rows = [e * cap + i for i in range(min(max(a[e], 0), cap))]
+        if not rows:
+            continue
+        nblk = -(-len(rows) // block_m)
+        sorted_ids[pos:pos + len(rows)] = rows
+        for b in range(nblk):
+            expert_ids[pos // block_m + b] = e
+        pos += nblk * block_m
+    return np.array(sorted_ids, np.int32), np.array(expert_ids, np.int32), pos

@@ -57,3 +57,32 @@ def test_capacity_bounds_every_routing():
         # worst case: every used expert leaves bm-1 padding slots
         used = min(experts, t * topk)
         assert cap >= t * topk + used * (bm - 1) and cap % bm == 0 and blocks * bm == cap
+
+
+# ---- grouped-contiguous and grouped-masked organizations ---------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("bm", [1, 4, 16, 128])
+def test_grouped_maps_equal_direct_construction(seed, bm):
+    rng = np.random.default_rng(seed)
+    e = int(rng.integers(1, 9))
+    cnt = rng.integers(0, 40, size=e)
+    cnt[rng.integers(0, e)] = 0                               # an empty expert
+    offs = np.concatenate([[0], np.cumsum(cnt)])
+    for got, ref in [(A.grouped_map("contiguous", offs, e, bm), A.grouped_map_direct("contiguous", offs, e, bm))]:
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]) and got[2] == ref[2]
+    cap = 32
+    counts = rng.integers(-3, 40, size=e)                     # clamped to [0, cap]
+    got = A.grouped_map("masked", counts, e, bm, cap)
+    ref = A.grouped_map_direct("masked", counts, e, bm, cap)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]) and got[2] == ref[2]
+
+
+def test_grouped_map_invariants():
+    offs = np.array([0, 5, 5, 12])
+    s, eid, npp = A.grouped_map("contiguous", offs, 3, 4)
+    assert npp == 8 + 8                                        # 5 -> 8, 0 -> 0, 7 -> 8
+    assert list(s[:8]) == [0, 1, 2, 3, 4, 12, 12, 12] and list(s[8:16]) == [5, 6, 7, 8, 9, 10, 11, 12]
+    assert list(eid[:4]) == [0, 0, 2, 2]
+    s, eid, npp = A.grouped_map("masked", np.array([2, 0, 3]), 3, 2, cap=4)
+    assert list(s[:npp]) == [0, 1, 8, 9, 10, 12] and list(eid[:3]) == [0, 2, 2]
