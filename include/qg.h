@@ -188,6 +188,36 @@ qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, in
                        int64_t cap_blocks, int32_t* num_post_pad, void* stream);
 
 /*
+ * The grouped MoE input organizations ("Humming" wiki article, "Device and workload
+ * selection": grouped-contiguous execution keeps each expert's rows together;
+ * grouped-masked execution gives each expert its own storage with a count of valid rows).
+ * Both name input rows directly: qg_moe_grouped_map writes the block map in qg_moe_align's
+ * contract (rows of each expert in ascending order, padded to block_m with the sentinel
+ * rows_total; the expert of every block; the padded total), after which
+ *     qg_moe_gemm(p, x, x_scale, sorted_ids, expert_ids, num_post_pad,
+ *                 rows_total, 1, block_m, y, ws, ws_bytes, stream)
+ * computes y[r] = x[r] . W_e^T for every row r of expert e; y has x's row layout and rows
+ * that belong to no expert are not written.
+ *   layout = QG_MOE_CONTIGUOUS: offsets_or_counts = device int32 [E+1], expert e owns rows
+ *            [offsets[e], offsets[e+1]) of x [rows_total][K]; offsets[0] = 0, non-decreasing,
+ *            offsets[E] <= rows_total (offsets are clamped to [0, rows_total] and made
+ *            non-decreasing on the device, so malformed offsets give a wrong map, never an
+ *            out-of-range write); rows_per_expert is ignored.
+ *   layout = QG_MOE_MASKED: offsets_or_counts = device int32 [E] valid-row counts (clamped to
+ *            [0, rows_per_expert]); x is [E][rows_per_expert][K] = [rows_total][K] with
+ *            rows_total = E * rows_per_expert (else QG_ERR_INVALID_ARG).
+ * Buffers as for qg_moe_align with capacities qg_moe_capacity(rows_total, 1, E, block_m)
+ * (QG_ERR_CAPACITY below them); block_m a power of two in [1, 256] (the GEMM then takes the
+ * block sizes qg_moe_gemm lists; qg_moe_block_m(p, rows, 1) picks one for about `rows`
+ * valid rows).  E <= 1024, rows_total <= 2^30.
+ */
+enum { QG_MOE_CONTIGUOUS = 1, QG_MOE_MASKED = 2 };
+qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, int32_t num_experts,
+                             int64_t rows_total, int64_t rows_per_expert, int32_t block_m, int32_t* sorted_ids,
+                             int64_t cap_sorted, int32_t* expert_ids, int64_t cap_blocks, int32_t* num_post_pad,
+                             void* stream);
+
+/*
  * qg_moe_gemm: grouped GEMM over the aligned rows.  For every (token t, slot j)
  * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
  *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3, else NULL

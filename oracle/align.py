@@ -95,17 +95,20 @@ def grouped_row_experts(layout: str, arr, experts: int, cap: int = 0) -> np.ndar
     return np.where(i < cnt[:, None], np.arange(experts)[:, None], -1).reshape(-1)
 
 
-def grouped_map(layout: str, arr, experts: int, block_m: int, cap: int = 0):
+def grouped_map(layout: str, arr, experts: int, block_m: int, cap: int = 0, rows_total: int | None = None):
     """(sorted_ids, expert_ids, num_post_pad) of a grouped organization, with the indexed path's
-    capacity for rows_total rows and topk = 1."""
+    capacity for rows_total rows and topk = 1.  Contiguous: rows_total defaults to offsets[E];
+    rows past offsets[E] belong to no expert."""
     ids = grouped_row_experts(layout, arr, experts, cap)
+    if rows_total is not None and rows_total > ids.size:
+        ids = np.concatenate([ids, np.full(rows_total - ids.size, -1, dtype=ids.dtype)])
     return moe_align(ids.reshape(-1, 1), experts, block_m)
 
 
-def grouped_map_direct(layout: str, arr, experts: int, block_m: int, cap: int = 0):
+def grouped_map_direct(layout: str, arr, experts: int, block_m: int, cap: int = 0, rows_total: int | None = None):
     """The same map written out expert by expert with loops, for pinning grouped_map."""
     a = [int(v) for v in np.asarray(arr).reshape(-1)]
-    total = a[experts] if layout == "contiguous" else experts * cap
+    total = (a[experts] if rows_total is None else rows_total) if layout == "contiguous" else experts * cap
     cs, cb = capacity(total, 1, experts, block_m)
     sorted_ids = [total] * cs
     expert_ids = [-1] * cb

@@ -4,8 +4,8 @@ Argument marshalling only: torch tensors supply device pointers, torch's current
 stream supplies the hipStream_t, and every step of the computation runs in the
 library's HIP kernels.  The entry points mirror include/qg.h one to one:
 ``prepared_bytes``, ``prepare``, ``workspace_bytes``, ``gemm``, ``moe_block_m``,
-``moe_capacity``, ``moe_align``, ``moe_gemm``, ``moe_swiglu``, ``moe_combine``, ``dequant``,
-``status_str``.
+``moe_capacity``, ``moe_align``, ``moe_grouped_map``, ``moe_gemm``, ``moe_swiglu``,
+``moe_combine``, ``dequant``, ``status_str``.
 
 There is no fallback: if libqg.so is missing or cannot be loaded, every call raises.
 """
@@ -23,11 +23,12 @@ S_F16, S_BF16, S_F32, S_UE8M0 = 1, 2, 3, 4
 A_F16, A_BF16, A_FP8_E4M3 = 1, 2, 3
 O_F16, O_BF16 = 1, 2
 C_NATIVE, C_W_TO_FP8 = 0, 1
+MOE_CONTIGUOUS, MOE_MASKED = 1, 2
 
 STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_ERR_ARCH_MISMATCH",
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
-           "qg_moe_align", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine", "qg_dequant", "qg_status_str",
+           "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine", "qg_dequant", "qg_status_str",
            "qg_version"]
 
 
@@ -73,6 +74,8 @@ def lib():
         L.qg_moe_capacity.restype = i32
         L.qg_moe_align.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, i64, vp, vp]
         L.qg_moe_align.restype = i32
+        L.qg_moe_grouped_map.argtypes = [i32, vp, i32, i64, i64, i32, vp, i64, vp, i64, vp, vp]
+        L.qg_moe_grouped_map.restype = i32
         L.qg_moe_gemm.argtypes = [pp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
         L.qg_moe_gemm.restype = i32
         L.qg_moe_swiglu.argtypes, L.qg_moe_swiglu.restype = [vp, i64, i64, i32, i32, vp, vp, vp], i32
@@ -159,6 +162,15 @@ def moe_align(topk_ids, tokens: int, topk: int, num_experts: int, block_m: int, 
     st = lib().qg_moe_align(_ptr(topk_ids), tokens, topk, num_experts, block_m, _ptr(sorted_ids), sorted_ids.numel(),
                             _ptr(expert_ids), expert_ids.numel(), _ptr(num_post_pad), _stream(stream))
     _check(st, "qg_moe_align")
+
+
+def moe_grouped_map(layout: int, offsets_or_counts, num_experts: int, rows_total: int, rows_per_expert: int,
+                    block_m: int, sorted_ids, expert_ids, num_post_pad, stream=None):
+    """Block map of a grouped-contiguous (offsets [E+1]) or grouped-masked (counts [E]) MoE input."""
+    st = lib().qg_moe_grouped_map(layout, _ptr(offsets_or_counts), num_experts, rows_total, rows_per_expert, block_m,
+                                  _ptr(sorted_ids), sorted_ids.numel(), _ptr(expert_ids), expert_ids.numel(),
+                                  _ptr(num_post_pad), _stream(stream))
+    _check(st, "qg_moe_grouped_map")
 
 
 def moe_gemm(p: Prepared, x, x_scale, sorted_ids, expert_ids, num_post_pad, tokens: int, topk: int, block_m: int,

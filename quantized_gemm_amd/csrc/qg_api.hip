@@ -488,6 +488,28 @@ qg_status qg_moe_align(const int32_t* topk_ids, int64_t tokens, int32_t topk, in
   return launched();
 }
 
+qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, int32_t num_experts, int64_t rows_total,
+                             int64_t rows_per_expert, int32_t block_m, int32_t* sorted_ids, int64_t cap_sorted,
+                             int32_t* expert_ids, int64_t cap_blocks, int32_t* num_post_pad, void* stream) {
+  if (layout != QG_MOE_CONTIGUOUS && layout != QG_MOE_MASKED) return QG_ERR_INVALID_ARG;
+  if (num_experts <= 0 || rows_total < 0) return QG_ERR_INVALID_ARG;
+  if (block_m <= 0 || block_m > 256 || (block_m & (block_m - 1)) != 0) return QG_ERR_INVALID_ARG;
+  if (layout == QG_MOE_MASKED && (rows_per_expert < 0 || rows_total != (int64_t)num_experts * rows_per_expert))
+    return QG_ERR_INVALID_ARG;
+  if (num_experts > 1024) return QG_ERR_UNSUPPORTED;
+  if (rows_total > (int64_t)1 << 30) return QG_ERR_UNSUPPORTED;
+  if (!offsets_or_counts || !sorted_ids || !expert_ids || !num_post_pad) return QG_ERR_INVALID_ARG;
+  int64_t cs, cb;
+  qg_moe_capacity(rows_total, 1, num_experts, block_m, &cs, &cb);
+  if (cap_sorted < cs || cap_blocks < cb) return QG_ERR_CAPACITY;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  if (!launch_grouped_map(offsets_or_counts, layout == QG_MOE_MASKED, num_experts, rows_total, (int)rows_per_expert,
+                          block_m, sorted_ids, cs, expert_ids, cb, num_post_pad, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
 qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
                       const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
                       int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream) {

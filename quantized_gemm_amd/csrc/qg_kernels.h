@@ -78,6 +78,12 @@ bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int ou
 bool launch_combine(const void* y, const float* w, const int32_t* ids, int64_t tokens, int topk, int experts, int64_t n,
                     int dtype, void* out, hipStream_t st);
 
+// Block map of the grouped-contiguous (offsets [E+1]) or grouped-masked (counts [E], cap rows
+// per expert) MoE input organizations; false if the expert count is beyond the kernel's limit.
+bool launch_grouped_map(const int32_t* arr, bool masked, int experts, int64_t rows_total, int cap, int block_m,
+                        int32_t* sorted_ids, int64_t cap_sorted, int32_t* expert_ids, int64_t cap_blocks,
+                        int32_t* num_post_pad, hipStream_t st);
+
 void launch_moe_align(const int32_t* ids, int tk, int experts, int block_m, int32_t* sorted_ids, int64_t cap_sorted,
                       int32_t* expert_ids, int64_t cap_blocks, int32_t* num_post_pad, hipStream_t st);
 

@@ -155,3 +155,15 @@ def test_reduction_length_rules():
     assert qg.prepared_bytes(_desc(k=1408)) > 0
     assert qg.prepared_bytes(_desc(k=1344, group_k=64)) == 0
     assert qg.prepared_bytes(_desc(k=1344, group_k=0)) == 0
+
+
+def test_grouped_map_rejects_on_the_host():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    cs, cb = A.capacity(100, 1, 8, 16)
+    assert lib.qg_moe_grouped_map(3, fake, 8, 100, 0, 16, fake, cs, fake, cb, fake, None) == 1   # bad layout
+    assert lib.qg_moe_grouped_map(1, fake, 8, 100, 0, 12, fake, cs, fake, cb, fake, None) == 1   # block not 2^n
+    assert lib.qg_moe_grouped_map(2, fake, 8, 100, 16, 16, fake, cs, fake, cb, fake, None) == 1  # 8 * 16 != 100
+    assert lib.qg_moe_grouped_map(1, fake, 2000, 100, 0, 16, fake, cs, fake, cb, fake, None) == 2  # too many experts
+    assert lib.qg_moe_grouped_map(1, fake, 8, 100, 0, 16, fake, cs - 1, fake, cb, fake, None) == 6
+    assert lib.qg_moe_grouped_map(1, None, 8, 100, 0, 16, fake, cs, fake, cb, fake, None) == 1

@@ -69,7 +69,9 @@ def test_grouped_maps_equal_direct_construction(seed, bm):
     cnt = rng.integers(0, 40, size=e)
     cnt[rng.integers(0, e)] = 0                               # an empty expert
     offs = np.concatenate([[0], np.cumsum(cnt)])
-    for got, ref in [(A.grouped_map("contiguous", offs, e, bm), A.grouped_map_direct("contiguous", offs, e, bm))]:
+    for extra in (None, int(offs[-1]) + 7):                  # trailing rows of no expert
+        got = A.grouped_map("contiguous", offs, e, bm, rows_total=extra)
+        ref = A.grouped_map_direct("contiguous", offs, e, bm, rows_total=extra)
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]) and got[2] == ref[2]
     cap = 32
     counts = rng.integers(-3, 40, size=e)                     # clamped to [0, cap]
