@@ -68,7 +68,14 @@ enum { QG_A_F16 = 1, QG_A_BF16 = 2, QG_A_FP8_E4M3 = 3 };
 enum { QG_O_F16 = 1, QG_O_BF16 = 2 };
 /* Compute options. */
 enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                               */
-       QG_C_W_TO_FP8 = 1   /* int4 weights converted to e4m3 in-kernel (FP8 activations)      */ };
+       QG_C_W_TO_FP8 = 1,  /* int4 weights converted to e4m3 in-kernel (FP8 activations)      */
+       /* Flag, OR-ed into either option: batch-invariant execution ("Humming" wiki article,
+        * "Precision and deployment considerations": no Stream-K-style split and the same
+        * MMA type across batch sizes).  Every row count then runs the MFMA kernel without a
+        * split over K, so each output row is bitwise the same whatever M (or T) and the other
+        * rows are; slower at small M.  MoE block sizes below 128 are rejected.  W4A8 layers
+        * must be given (or denied) the widening workspace consistently across calls. */
+       QG_C_BATCH_INVARIANT = 4 };
 
 /*
  * Layer description ("Layer config": shapes, data types, quantization parameters).
@@ -86,7 +93,7 @@ typedef struct {
   int32_t group_k;      /* elements per scale along K; 0 = one scale per output channel */
   int32_t has_zero;     /* 1: uint4 zero point per (n, group), only with QG_W_UINT4    */
   int32_t a_type;       /* QG_A_*                                                      */
-  int32_t compute;      /* QG_C_*                                                      */
+  int32_t compute;      /* QG_C_NATIVE or QG_C_W_TO_FP8, optionally | QG_C_BATCH_INVARIANT */
   int32_t out_type;     /* QG_O_*                                                      */
   int32_t num_experts;  /* 1 for a dense layer                                         */
   int64_t n;            /* output features                                             */

@@ -22,7 +22,7 @@ W_INT4, W_UINT4, W_FP4_E2M1, W_FP8_E4M3 = 1, 2, 3, 4
 S_F16, S_BF16, S_F32, S_UE8M0 = 1, 2, 3, 4
 A_F16, A_BF16, A_FP8_E4M3 = 1, 2, 3
 O_F16, O_BF16 = 1, 2
-C_NATIVE, C_W_TO_FP8 = 0, 1
+C_NATIVE, C_W_TO_FP8, C_BATCH_INVARIANT = 0, 1, 4
 MOE_CONTIGUOUS, MOE_MASKED = 1, 2
 
 STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_ERR_ARCH_MISMATCH",

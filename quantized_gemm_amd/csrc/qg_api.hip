@@ -63,6 +63,7 @@ struct PathInfo {
   int w4;         // 4-bit codes
   int af, of, st;
   int dq_wp;      // path used for the read-back check
+  int binv;       // batch-invariant: MFMA kernel for every row count, no split over K
 };
 
 int scale_bytes(int s_type) {
@@ -75,8 +76,13 @@ int scale_bytes(int s_type) {
 }
 
 // Host-only validation of a layer description.
-qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
-  if (!d) return QG_ERR_INVALID_ARG;
+qg_status check_desc(const qg_layer_desc* dd, PathInfo* pi) {
+  if (!dd) return QG_ERR_INVALID_ARG;
+  // the batch-invariant flag only steers the selector; validate the rest without it
+  qg_layer_desc dv = *dd;
+  const int binv = (dv.compute & QG_C_BATCH_INVARIANT) != 0;
+  dv.compute &= ~QG_C_BATCH_INVARIANT;
+  const qg_layer_desc* d = &dv;
   if (d->w_type < QG_W_INT4 || d->w_type > QG_W_FP8_E4M3) return QG_ERR_INVALID_ARG;
   if (d->s_type < QG_S_F16 || d->s_type > QG_S_UE8M0) return QG_ERR_INVALID_ARG;
   if (d->a_type < QG_A_F16 || d->a_type > QG_A_FP8_E4M3) return QG_ERR_INVALID_ARG;
@@ -129,6 +135,7 @@ qg_status check_desc(const qg_layer_desc* d, PathInfo* pi) {
     p.wp_small = WP_FP8; p.w4 = 0; p.af = A_FP8; p.st = S_F32; p.dq_wp = WP_FP8;
   }
   p.wp_mfma = p.wp_small == WP_INT4Q_MAGIC ? WP_INT4Q_FP8 : p.wp_small;
+  p.binv = binv;
   if (pi) *pi = p;
   return QG_OK;
 }
@@ -205,7 +212,7 @@ bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8; }
 // int4 -> e4m3 kernel.
 constexpr int kMaxSplit = 8;
 int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
-  if (pi.wp_mfma == WP_INT4Q_FP8 || tiles * 2 > kCUs) return 1;
+  if (pi.wp_mfma == WP_INT4Q_FP8 || pi.binv || tiles * 2 > kCUs) return 1;
   const int64_t bk = pi.af == A_FP8 ? 128 : 64;   // K per step: fp8 MFMAs take 128
   const int64_t steps = k / bk;
   int sp = 1;
@@ -229,7 +236,7 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   t.ksplit = t.bm == 128 ? split_for(tiles, k, group, pi) : 1;
   // experiment-only override of the split (QG_KSPLIT=1|2|4|8; slices must stay whole groups)
   static const char* ks = getenv("QG_KSPLIT");
-  if (ks && t.bm == 128 && pi.wp_mfma != WP_INT4Q_FP8) {
+  if (ks && t.bm == 128 && pi.wp_mfma != WP_INT4Q_FP8 && !pi.binv) {
     const int v = atoi(ks);
     const int64_t bk = pi.af == A_FP8 ? 128 : 64;
     if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / bk) % v == 0 && (group <= 0 || (k / v) % group == 0))
@@ -274,7 +281,7 @@ int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
 
 // Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
-  if (m <= kStreamMaxRows) {
+  if (m <= kStreamMaxRows && !pi.binv) {
     const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
     return sp > 1 ? (size_t)sp * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
   }
@@ -389,7 +396,8 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
-  if (m > kStreamMaxRows && is_w4a8(pi) && widen_ok(p, m, ws, ws_bytes)) {
+  const bool mfma = m > kStreamMaxRows || pi.binv;   // batch-invariant: one MMA type for every M
+  if (mfma && is_w4a8(pi) && widen_ok(p, m, ws, ws_bytes)) {
     const PathInfo pw = widened_path(pi);
     MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pw);
     t.ksplit = 1;
@@ -401,7 +409,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
       return QG_ERR_UNSUPPORTED;
     return launched();
   }
-  if (m > kStreamMaxRows) {
+  if (mfma) {
     const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
     if (t.ksplit > 1) {
       const size_t need = dense_workspace(p, pi, m);
@@ -449,6 +457,7 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   // which costs more than the occasional second pass over an expert's weights).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
+  if (pi.binv) return (mean < 512 || !mfma_rows256(pi)) ? 128 : 256;   // MFMA blocks at every size
   if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
     if (mean <= 16) return 16;
@@ -524,6 +533,7 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   if (block_m != 4 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256)
     return QG_ERR_UNSUPPORTED;
   if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
+  if (pi.binv && block_m <= kStreamMaxRows) return QG_ERR_UNSUPPORTED;   // one MMA type for every size
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;

@@ -18,10 +18,10 @@ _O = {"f16": O_F16, "bf16": O_BF16}
 _TORCH_OUT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def desc_for(layer):
+def desc_for(layer, compute_flags: int = 0):
     return make_desc(_W[layer.w_type], _S[layer.s_type], layer.group, layer.z is not None, _A[layer.a_type],
-                     C_W_TO_FP8 if layer.compute == "w_to_fp8" else C_NATIVE, _O[layer.out_type], layer.experts,
-                     layer.n, layer.k)
+                     (C_W_TO_FP8 if layer.compute == "w_to_fp8" else C_NATIVE) | compute_flags, _O[layer.out_type],
+                     layer.experts, layer.n, layer.k)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -34,12 +34,13 @@ def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
-def prepare_layer(layer, device="cuda", stream=None):
+def prepare_layer(layer, device="cuda", stream=None, compute_flags: int = 0):
     """Upload the logical tensors, run qg_prepare, return (handle, prepared buffer).
 
-    The logical tensors are released after the stream has passed the transform.
+    compute_flags are OR-ed into the compute option (e.g. C_BATCH_INVARIANT).  The logical
+    tensors are released after the stream has passed the transform.
     """
-    desc = desc_for(layer)
+    desc = desc_for(layer, compute_flags)
     nbytes = prepared_bytes(desc)
     if nbytes == 0:
         raise ValueError(f"unsupported layer {layer.name}")

@@ -167,3 +167,10 @@ def test_grouped_map_rejects_on_the_host():
     assert lib.qg_moe_grouped_map(1, fake, 2000, 100, 0, 16, fake, cs, fake, cb, fake, None) == 2  # too many experts
     assert lib.qg_moe_grouped_map(1, fake, 8, 100, 0, 16, fake, cs - 1, fake, cb, fake, None) == 6
     assert lib.qg_moe_grouped_map(1, None, 8, 100, 0, 16, fake, cs, fake, cb, fake, None) == 1
+
+
+def test_batch_invariant_flag_is_a_selector_option():
+    base = qg.prepared_bytes(_desc())
+    assert qg.prepared_bytes(_desc(compute=qg.C_NATIVE | qg.C_BATCH_INVARIANT)) == base
+    assert qg.prepared_bytes(_desc(compute=2)) == 0
+    assert qg.prepared_bytes(_desc(compute=8)) == 0
