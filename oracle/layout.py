@@ -21,7 +21,8 @@ W: 16-byte units indexed [e][nb = n/16][ku = k/KU][c = n%16], KU = 32 for 4-bit
    int4 for the e4m3 conversion -> c (two's complement); e2m1 -> c.
    e4m3 unit: 16 bytes, element k = ku*16 + i at byte i.
 S: elements [e][nb][g][c] = scale[e][nb*16 + c][g] in the scale type's own bytes
-   (2 for f16/bf16, 4 for f32, 1 for UE8M0); channel scales have G = 1.
+   (2 for f16/bf16, 4 for f32, 1 for UE8M0); channel scales have G = 1.  Block scales of
+   e4m3 weights (one per G x G block of output channels x K): [e][n/G][g] as given.
 Z: for each [e][nb][g] two u32 words; column c at word c/8, nibble c%8.
 """
 from __future__ import annotations
@@ -52,7 +53,8 @@ def sizes(w_type, s_type, n, k, group, experts, has_zero):
     bits = 8 if w_type == "e4m3" else 4
     g = 1 if group == 0 else k // group
     wb = experts * n * k * bits // 8
-    sb = experts * n * g * SCALE_BYTES[s_type]
+    block = w_type == "e4m3" and group > 0          # block scales [e][n/G][k/G], stored as given
+    sb = experts * (n // group if block else n) * g * SCALE_BYTES[s_type]
     zb = experts * (n // 16) * g * 8 if has_zero else 0
     off_s = _align(wb)
     off_z = off_s + _align(sb)
@@ -96,10 +98,13 @@ def repack(layer) -> np.ndarray:
             words |= v[..., order[p]] << np.uint32(4 * p)
         units = words.transpose(0, 1, 3, 2, 4)       # e, nb, ku, c, j
         out[:sz["w_bytes"]] = np.ascontiguousarray(units).astype("<u4").view(np.uint8).reshape(-1)
-    # scales: [e][nb][g][c]
+    # scales: [e][nb][g][c] (block scales: [e][n/G][g] as given)
     g = sz["groups"]
     s = np.asarray(layer.s)
-    s = s.reshape(e_, nb, 16, g).transpose(0, 1, 3, 2)
+    if layer.w_type == "e4m3" and layer.group > 0:
+        s = s.reshape(e_, n // layer.group, g)
+    else:
+        s = s.reshape(e_, nb, 16, g).transpose(0, 1, 3, 2)
     sdt = {"f16": "<u2", "bf16": "<u2", "f32": "<f4", "ue8m0": "u1"}[layer.s_type]
     out[sz["off_s"]:sz["off_s"] + sz["s_bytes"]] = np.ascontiguousarray(s).astype(sdt).view(np.uint8).reshape(-1)
     if has_zero:
@@ -142,8 +147,11 @@ def unpack(buf, w_type, a_type, s_type, n, k, group, experts, has_zero):
                 w |= r[..., i] << np.uint32(4 * i)
     g = sz["groups"]
     sdt = {"f16": "<u2", "bf16": "<u2", "f32": "<f4", "ue8m0": "u1"}[s_type]
-    sb = buf[sz["off_s"]:sz["off_s"] + sz["s_bytes"]].view(sdt).reshape(experts, nb, g, 16)
-    s = np.ascontiguousarray(sb.transpose(0, 1, 3, 2)).reshape(experts, n, g)
+    if w_type == "e4m3" and group > 0:
+        s = buf[sz["off_s"]:sz["off_s"] + sz["s_bytes"]].view(sdt).reshape(experts, n // group, g).copy()
+    else:
+        sb = buf[sz["off_s"]:sz["off_s"] + sz["s_bytes"]].view(sdt).reshape(experts, nb, g, 16)
+        s = np.ascontiguousarray(sb.transpose(0, 1, 3, 2)).reshape(experts, n, g)
     z = None
     if has_zero:
         zw = buf[sz["off_z"]:sz["off_z"] + sz["z_bytes"]].view("<u4").reshape(experts, nb, g, 2)

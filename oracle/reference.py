@@ -21,7 +21,11 @@ Passages followed:
 Readings where the pages are silent (each listed in the design notes):
 * zero points are integers in the code domain: w = (u - z) * s;
 * symmetric int4 keeps -8;
-* activations are what the kernel reads: f16/bf16 values, or sx[m] * e4m3(code);
+* activations are what the kernel reads: f16/bf16 values, or sx[m] * e4m3(code) (with block
+  scales sx[m, k / 128] * e4m3(code));
+* block scales ("Humming" wiki article, "Quantization representation": a scale shared across
+  both matrix dimensions): e4m3 weights with group G > 0 carry one scale per G x G block of
+  (output channel, K);
 * MoE output is [T, topk, N], one row per (token, slot); routing probabilities are
   not applied; slots whose id is outside [0, E) are left unwritten (NaN here).
 """
@@ -59,16 +63,31 @@ def dequant_codes(layer_w, layer_s, layer_z, w_type: str, s_type: str, group: in
     return vals * s_full
 
 
+def is_block_scaled(layer) -> bool:
+    """e4m3 weights with group > 0: one scale per group x group block of (output channel, K)."""
+    return layer.w_type == "e4m3" and layer.group > 0
+
+
+def _scale_rows(layer, expert: int, rows=None):
+    """Scales of the given output channels as [rows, G] (block scales repeat over the block's rows)."""
+    s = np.asarray(layer.s[expert])
+    if is_block_scaled(layer):
+        r = np.arange(layer.n) if rows is None else np.asarray(rows)
+        return s[r // layer.group]
+    return s if rows is None else s[np.asarray(rows)]
+
+
 def dequant_layer(layer, expert: int = 0) -> np.ndarray:
     z = None if layer.z is None else layer.z[expert]
-    return dequant_codes(layer.w[expert], layer.s[expert], z, layer.w_type, layer.s_type, layer.group, layer.k)
+    return dequant_codes(layer.w[expert], _scale_rows(layer, expert), z, layer.w_type, layer.s_type, layer.group,
+                         layer.k)
 
 
 def dequant_rows(layer, expert: int, rows) -> np.ndarray:
     """Dequantize only output channels ``rows`` of one expert (for sampled checks at full size)."""
     rows = np.asarray(rows)
     z = None if layer.z is None else layer.z[expert][rows]
-    return dequant_codes(layer.w[expert][rows], layer.s[expert][rows], z,
+    return dequant_codes(layer.w[expert][rows], _scale_rows(layer, expert, rows), z,
                          layer.w_type, layer.s_type, layer.group, layer.k)
 
 
@@ -76,7 +95,11 @@ def activations(acts, a_type: str) -> np.ndarray:
     """The activation values the kernel multiplies, in float64 [M, K]."""
     x = F.decode_act(acts.x, a_type)
     if a_type == "e4m3":
-        x = x * np.asarray(acts.x_scale, dtype=np.float32).astype(np.float64)[:, None]
+        sx = np.asarray(acts.x_scale, dtype=np.float32).astype(np.float64)
+        if sx.ndim == 2:                       # one scale per (row, group of K / G columns)
+            x = x * np.repeat(sx, x.shape[1] // sx.shape[1], axis=1)
+        else:
+            x = x * sx[:, None]
     return x
 
 

@@ -187,6 +187,49 @@ def dense_w8a8_fp8(m: int = 1, n: int = 7168, k: int = 7168, seed: int = 0):
     return layer, Acts(xq, sx, None)
 
 
+def absmax_e4m3_blocks(x: np.ndarray, br: int, bc: int):
+    """Absmax e4m3 quantization per br x bc block of a 2-D array (rows, columns divisible):
+    returns (codes uint8 like x, scales float32 [R/br, C/bc]); each block quantized like one
+    row of absmax_e4m3_rows."""
+    r, c = x.shape
+    blocks = np.asarray(x, np.float32).reshape(r // br, br, c // bc, bc).transpose(0, 2, 1, 3).reshape(-1, br * bc)
+    q, sc = absmax_e4m3_rows(blocks)
+    q = q.reshape(r // br, c // bc, br, bc).transpose(0, 2, 1, 3).reshape(r, c)
+    return np.ascontiguousarray(q), sc.reshape(r // br, c // bc)
+
+
+def dense_w8a8_fp8_block(m: int = 16, n: int = 7168, k: int = 7168, block: int = 128, seed: int = 0):
+    """Dense W8A8 with block scales: e4m3 weights of N(0, 0.02) quantized per block x block tile
+    (absmax, float32 scales [N/block, K/block]); e4m3 activations of N(0,1) rows quantized per
+    (row, block of K) (float32 scales [M, K/block])."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_blocks(rng.standard_normal((m, k), dtype=np.float32), 1, block)
+    wf = (rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    wq, sw = absmax_e4m3_blocks(wf, block, block)
+    layer = Layer("dense_w8a8_fp8_block", "e4m3", "e4m3", "f32", "bf16", n, k, block, 1,
+                  wq.reshape(1, n, k), sw.reshape(1, n // block, k // block), None)
+    return layer, Acts(xq, sx, None)
+
+
+def moe_w8a8_fp8_block(t: int = 16, experts: int = 8, topk: int = 2, n: int = 256, k: int = 512, block: int = 128,
+                       seed: int = 0):
+    """MoE W8A8 with block scales (as dense_w8a8_fp8_block, per expert), softmax top-k routing of
+    N(0,1) logits."""
+    rng = _rng(seed)
+    xq, sx = absmax_e4m3_blocks(rng.standard_normal((t, k), dtype=np.float32), 1, block)
+    ws, ss = [], []
+    for _ in range(experts):
+        wf = (rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+        q, sc = absmax_e4m3_blocks(wf, block, block)
+        ws.append(q)
+        ss.append(sc)
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    layer = Layer("moe_w8a8_fp8_block", "e4m3", "e4m3", "f32", "bf16", n, k, block, experts,
+                  np.stack(ws), np.stack(ss), None)
+    return layer, Acts(xq, sx, ids, router_weights(logits, ids))
+
+
 def moe_w8a8_fp8(t: int = 16, experts: int = 8, topk: int = 2, n: int = 256, k: int = 512, seed: int = 0):
     """MoE W8A8: per-token absmax e4m3 activations, per-(expert, channel) absmax e4m3 weights
     (N(0, 0.02)), softmax top-k routing of N(0,1) logits."""
@@ -343,4 +386,5 @@ WORKLOADS = {
     "moe_w4a8_int4": moe_w4a8_int4,
     "dense_w4a8_mxfp4": dense_w4a8_mxfp4,
     "moe_w4a8_mxfp4": moe_w4a8_mxfp4,
+    "dense_w8a8_fp8_block": dense_w8a8_fp8_block,
 }

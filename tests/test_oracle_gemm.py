@@ -228,3 +228,44 @@ def test_w4a8_mxfp4_reduces_to_w4a16_mxfp4_on_the_same_values():
     x16 = synth.f32_to_bf16_bits(F.decode_e4m3(acts.x).astype(np.float32))
     l16 = synth.Layer("t", "e2m1", "bf16", "ue8m0", "bf16", 32, 256, 32, 1, layer.w, layer.s, None)
     assert np.array_equal(R.dense_reference(layer, acts), R.dense_reference(l16, synth.Acts(x16, None, None)))
+
+
+# ---- block-scaled e4m3 (scales over 128 x 128 weight blocks and 1 x 128 activation groups) ----
+
+def test_block_scaled_brute_force_is_exact():
+    layer, acts = synth.dense_w8a8_fp8_block(m=3, n=256, k=256, seed=6)
+    rng = np.random.default_rng(6)
+    layer.s = (2.0 ** rng.integers(-9, -4, size=layer.s.shape)).astype(np.float32)   # powers of two: exact
+    acts.x_scale = (2.0 ** rng.integers(-3, 2, size=acts.x_scale.shape)).astype(np.float32)
+    y = R.dense_reference(layer, acts)
+    wv = F.decode_e4m3(layer.w[0])
+    xv = F.decode_e4m3(acts.x)
+    ref = np.zeros((3, 256))
+    for m in range(3):
+        for n in range(256):
+            for k in range(256):
+                ref[m, n] += (xv[m, k] * float(acts.x_scale[m, k // 128])) * (wv[n, k] * float(layer.s[0, n // 128, k // 128]))
+    assert np.array_equal(y, ref)
+
+
+def test_block_scaled_uniform_scales_reduce_to_channel_scales():
+    layer, acts = synth.dense_w8a8_fp8_block(m=4, n=256, k=384, seed=7)
+    layer.s = np.full(layer.s.shape, 0.0078125, np.float32)
+    acts.x_scale = np.repeat(np.array([[0.5], [0.25], [2.0], [1.0]], np.float32), 3, axis=1)
+    ch = synth.Layer("t", "e4m3", "e4m3", "f32", "bf16", 256, 384, 0, 1, layer.w, np.full((1, 256, 1), 0.0078125, np.float32), None)
+    ych = R.dense_reference(ch, synth.Acts(acts.x, acts.x_scale[:, 0].copy(), None))
+    assert np.array_equal(R.dense_reference(layer, acts), ych)
+
+
+def test_block_quantizer_scales_each_block_by_its_own_absmax():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((256, 384)).astype(np.float32)
+    x[:128, 128:256] *= 100.0                                 # one loud block
+    q, s = synth.absmax_e4m3_blocks(x, 128, 128)
+    for bi in range(2):
+        for bj in range(3):
+            blk = x[128 * bi:128 * (bi + 1), 128 * bj:128 * (bj + 1)]
+            assert s[bi, bj] == np.float32(np.max(np.abs(blk)) / np.float32(448.0))
+            qb = F.decode_e4m3(q[128 * bi:128 * (bi + 1), 128 * bj:128 * (bj + 1)])
+            assert np.max(np.abs(qb)) == 448.0
+            assert np.max(np.abs(qb * float(s[bi, bj]) - blk)) <= 2.0 ** -4 * np.max(np.abs(blk)) + 1e-6

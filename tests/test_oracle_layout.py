@@ -93,3 +93,11 @@ def test_synthetic_fp8_inputs_are_nearest_even_e4m3_of_absmax_scaled_rows():
     back = F.decode_e4m3(codes) * scale[:, None]
     err = np.abs(back - x)
     assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) + 1e-30)
+
+
+def test_block_scaled_layout_round_trip():
+    layer, _ = synth.moe_w8a8_fp8_block(t=2, experts=2, topk=1, n=256, k=256, seed=3)
+    buf = L.repack(layer)
+    w, s, z = L.unpack(buf, layer.w_type, layer.a_type, layer.s_type, layer.n, layer.k, layer.group, layer.experts, False)
+    assert np.array_equal(w, layer.w) and np.array_equal(s, layer.s) and z is None
+    assert buf.size == L.sizes("e4m3", "f32", 256, 256, 128, 2, False)["total"]
