@@ -128,11 +128,13 @@ qg_status check_desc(const qg_layer_desc* dd, PathInfo* pi) {
     }
     p.wp_small = WP_FP4; p.order = 0; p.w4 = 1; p.st = S_UE8M0;
     p.dq_wp = WP_FP4;
-  } else {  // e4m3
-    if (d->a_type != QG_A_FP8_E4M3 || d->compute != QG_C_NATIVE || d->has_zero || d->group_k != 0 ||
-        d->s_type != QG_S_F32)
+  } else {  // e4m3: channel scales (group 0) or 128 x 128 block scales (group 128)
+    if (d->a_type != QG_A_FP8_E4M3 || d->compute != QG_C_NATIVE || d->has_zero ||
+        (d->group_k != 0 && d->group_k != 128) || d->s_type != QG_S_F32)
       return QG_ERR_UNSUPPORTED;
-    p.wp_small = WP_FP8; p.w4 = 0; p.af = A_FP8; p.st = S_F32; p.dq_wp = WP_FP8;
+    if (d->group_k == 128 && d->n % 128 != 0) return QG_ERR_UNSUPPORTED;
+    p.wp_small = d->group_k == 128 ? WP_FP8_BLOCK : WP_FP8; p.w4 = 0; p.af = A_FP8; p.st = S_F32;
+    p.dq_wp = WP_FP8;
   }
   p.wp_mfma = p.wp_small == WP_INT4Q_MAGIC ? WP_INT4Q_FP8 : p.wp_small;
   p.binv = binv;
@@ -148,6 +150,7 @@ Sizes sizes_of(const qg_layer_desc* d) {
   s.groups = d->group_k == 0 ? 1 : d->k / d->group_k;
   s.wb = d->n * d->k * bits / 8;                     // per expert
   s.sb = d->n * s.groups * scale_bytes(d->s_type);   // per expert
+  if (d->w_type == QG_W_FP8_E4M3 && d->group_k > 0) s.sb = (d->n / d->group_k) * s.groups * 4;   // block scales
   s.zb = d->has_zero ? (d->n / 16) * s.groups * 8 : 0;
   const int64_t e = d->num_experts;
   s.off_s = align256(e * s.wb);
@@ -279,8 +282,30 @@ int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
   return sp;
 }
 
+// Block-scaled e4m3: one kernel (128 x 256 tiles, a promotion per 128-wide step) for every
+// row count; dense grids with at most half a workgroup per CU split K over up to 8
+// workgroups (whole steps, at least two per slice), the batch-invariant flag excepted.
+bool is_block(const PathInfo& pi) { return pi.wp_small == WP_FP8_BLOCK; }
+MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
+  MfmaTile t{};
+  t.bm = 128;
+  const int64_t tiles = ((rows + 127) / 128) * ((n + 255) / 256);
+  t.grid_x = (unsigned)tiles;
+  t.grid_y = 1;
+  t.ksplit = 1;
+  const int64_t steps = k / 128;
+  if (!pi.binv)
+    while (t.ksplit < 8 && tiles * t.ksplit * 2 <= kCUs && steps % (t.ksplit * 2) == 0 && steps / (t.ksplit * 2) >= 2)
+      t.ksplit *= 2;
+  return t;
+}
+
 // Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
+  if (is_block(pi)) {
+    const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
+    return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
+  }
   if (m <= kStreamMaxRows && !pi.binv) {
     const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
     return sp > 1 ? (size_t)sp * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
@@ -336,6 +361,7 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
   if (!desc->has_zero) a.z = nullptr;
   a.experts = desc->num_experts; a.n = (int)desc->n; a.k = (int)desc->k; a.groups = (int)sz.groups;
   a.w4 = pi.w4; a.order = pi.order; a.bias8 = pi.bias8; a.s_bytes = scale_bytes(desc->s_type);
+  a.s_plain = pi.wp_small == WP_FP8_BLOCK ? sz.sb / 4 * desc->num_experts : 0;
   launch_repack(a, (hipStream_t)stream);
   s = launched();
   if (s != QG_OK) return s;
@@ -396,6 +422,21 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
+  if (is_block(pi)) {
+    const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
+    if (t.ksplit > 1) {
+      const size_t need = dense_workspace(p, pi, m);
+      if (!ws || !aligned16(ws) || ws_bytes < need) return QG_ERR_WORKSPACE;
+      a.part = (float*)ws;
+      a.ksplit = t.ksplit;
+    }
+    QG_LOG("gemm m=%lld n=%lld k=%lld -> fp8 block-scaled grid=%u ksplit=%d", (long long)m, (long long)p->desc.n,
+           (long long)p->desc.k, t.grid_x, t.ksplit);
+    if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, false, false, (hipStream_t)stream))
+      return QG_ERR_UNSUPPORTED;
+    if (t.ksplit > 1 && !launch_split_reduce(a, false, false, pi.of, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
   const bool mfma = m > kStreamMaxRows || pi.binv;   // batch-invariant: one MMA type for every M
   if (mfma && is_w4a8(pi) && widen_ok(p, m, ws, ws_bytes)) {
     const PathInfo pw = widened_path(pi);
@@ -457,6 +498,7 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   // which costs more than the occasional second pass over an expert's weights).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
+  if (is_block(pi)) return 128;                  // the block-scaled kernel's only tile
   if (pi.binv) return (mean < 512 || !mfma_rows256(pi)) ? 128 : 256;   // MFMA blocks at every size
   if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
@@ -534,6 +576,7 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     return QG_ERR_UNSUPPORTED;
   if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (pi.binv && block_m <= kStreamMaxRows) return QG_ERR_UNSUPPORTED;   // one MMA type for every size
+  if (is_block(pi) && block_m != 128) return QG_ERR_UNSUPPORTED;
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
@@ -621,6 +664,7 @@ qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* str
   PathInfo pi;
   qg_status s = check_prepared(p, &pi);
   if (s != QG_OK) return s;
+  if (is_block(pi)) return QG_ERR_UNSUPPORTED;   // block scales: the layout check is the byte image
   if (expert < 0 || expert >= p->desc.num_experts || !out) return QG_ERR_INVALID_ARG;
   s = check_arch();
   if (s != QG_OK) return s;

@@ -38,7 +38,8 @@ enum : int {
   WP_INT4Q_MAGIC = 2,  // int4 (QUAD order, two's complement) -> 16-bit operand, A permuted to match
   WP_FP4 = 3,          // e2m1 -> bf16/f16 with the UE8M0 block scale folded in
   WP_FP8 = 4,          // e4m3 used as is, fp8 MFMA
-  WP_INT4Q_FP8 = 5     // int4 (QUAD) -> e4m3 by table, fp8 MFMA, group scale per 128-k MFMA
+  WP_INT4Q_FP8 = 5,    // int4 (QUAD) -> e4m3 by table, fp8 MFMA, group scale per 128-k MFMA
+  WP_FP8_BLOCK = 6     // e4m3 with 128 x 128 block scales x e4m3 with (row, 128-k) scales, promoted per step
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

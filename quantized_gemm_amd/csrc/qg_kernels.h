@@ -62,6 +62,7 @@ struct RepackArgs {
   int order;                 // 0 natural, 1 pair, 2 quad
   int bias8;                 // xor every nibble with 8
   int s_bytes;               // bytes per scale element
+  int64_t s_plain;           // > 0: block scales, this many 4-byte elements copied as they are
 };
 void launch_repack(const RepackArgs& a, hipStream_t st);
 

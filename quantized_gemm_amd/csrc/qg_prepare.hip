@@ -48,12 +48,17 @@ __global__ void repack_w_kernel(RepackArgs a) {
   *(u32x4*)(a.out_w + (u << 4)) = v;
 }
 
-// One thread per scale element: [e][nb][g][c] <- [e][nb*16 + c][g].
+// One thread per scale element: [e][nb][g][c] <- [e][nb*16 + c][g]; block scales
+// (s_plain elements, 4 bytes each) are copied as they are.
 __global__ void repack_s_kernel(RepackArgs a) {
   const int nb_count = a.n >> 4;
-  const int64_t total = (int64_t)a.experts * a.n * a.groups;
+  const int64_t total = a.s_plain > 0 ? a.s_plain : (int64_t)a.experts * a.n * a.groups;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
+  if (a.s_plain > 0) {
+    ((uint32_t*)a.out_s)[i] = ((const uint32_t*)a.s)[i];
+    return;
+  }
   const int c = (int)(i & 15);
   int64_t rest = i >> 4;
   const int g = (int)(rest % a.groups);
@@ -91,7 +96,7 @@ void launch_repack(const RepackArgs& a, hipStream_t st) {
   const int64_t kun = a.w4 ? (a.k >> 5) : (a.k >> 4);
   const int64_t units = (int64_t)a.experts * (a.n >> 4) * kun * 16;
   hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, a);
-  const int64_t ns = (int64_t)a.experts * a.n * a.groups;
+  const int64_t ns = a.s_plain > 0 ? a.s_plain : (int64_t)a.experts * a.n * a.groups;
   hipLaunchKernelGGL(repack_s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, a);
   if (a.z) {
     const int64_t nz = (int64_t)a.experts * (a.n >> 4) * a.groups * 2;

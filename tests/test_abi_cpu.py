@@ -174,3 +174,15 @@ def test_batch_invariant_flag_is_a_selector_option():
     assert qg.prepared_bytes(_desc(compute=qg.C_NATIVE | qg.C_BATCH_INVARIANT)) == base
     assert qg.prepared_bytes(_desc(compute=2)) == 0
     assert qg.prepared_bytes(_desc(compute=8)) == 0
+
+
+def test_block_scaled_fp8_sizes_match_layout_reference():
+    layer, _ = synth.moe_w8a8_fp8_block(t=2, experts=3, topk=1, n=256, k=512, seed=1)
+    d = layers.desc_for(layer)
+    sz = L.sizes("e4m3", "f32", 256, 512, 128, 3, False)
+    assert qg.prepared_bytes(d) == sz["total"]
+    # only 128 x 128 blocks, and N a multiple of the block
+    assert qg.prepared_bytes(_desc(w_type=qg.W_FP8_E4M3, s_type=qg.S_F32, group_k=256, has_zero=0,
+                                   a_type=qg.A_FP8_E4M3)) == 0
+    assert qg.prepared_bytes(_desc(w_type=qg.W_FP8_E4M3, s_type=qg.S_F32, group_k=128, has_zero=0,
+                                   a_type=qg.A_FP8_E4M3, n=448)) == 0
