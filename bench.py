@@ -48,6 +48,9 @@ WORKLOADS = {
     "moe_w4a16_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="bf16", moe=dict(experts=128, topk=8),
                             desc="MoE W4A16 MXFP4 (e2m1 + UE8M0/32), E=128 top-8, fused gate+up N=4096, K=7168, "
                                  "bf16 activations; T sweep"),
+    "dense_w8a8_fp8_block": dict(sweep=[1, 64, 512, 4096], n=7168, k=7168, dtype="fp8",
+                                 desc="dense W8A8 e4m3 with 128 x 128 weight-block scales and per-(token, 128-K) "
+                                      "activation scales, bf16 output; M sweep"),
     "dense_w4a8_mxfp4": dict(sweep=[1, 16, 128, 1024, 4096], n=8192, k=8192, dtype="fp8",
                              desc="dense W4A8 MXFP4 (e2m1 + UE8M0/32 weights x per-token e4m3 activations, scaled "
                                   "fp8 x fp4 MFMAs), N=K=8192; M sweep"),

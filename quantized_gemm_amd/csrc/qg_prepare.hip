@@ -48,13 +48,24 @@ __global__ void repack_w_kernel(RepackArgs a) {
   *(u32x4*)(a.out_w + (u << 4)) = v;
 }
 
+// Elements of a region padded to its 256-byte boundary (the bytes up to it are written too,
+// as zeros, so the prepared image is fully defined).
+inline int64_t padded_elems(int64_t elems, int bytes) { return (elems * bytes + 255) / 256 * 256 / bytes; }
+
 // One thread per scale element: [e][nb][g][c] <- [e][nb*16 + c][g]; block scales
-// (s_plain elements, 4 bytes each) are copied as they are.
-__global__ void repack_s_kernel(RepackArgs a) {
+// (s_plain elements, 4 bytes each) are copied as they are; then zeros up to the region's end.
+__global__ void repack_s_kernel(RepackArgs a, int64_t padded) {
   const int nb_count = a.n >> 4;
   const int64_t total = a.s_plain > 0 ? a.s_plain : (int64_t)a.experts * a.n * a.groups;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
+  if (i >= padded) return;
+  if (i >= total) {
+    const int eb = a.s_plain > 0 ? 4 : a.s_bytes;
+    if (eb == 1) a.out_s[i] = 0;
+    else if (eb == 2) ((uint16_t*)a.out_s)[i] = 0;
+    else ((uint32_t*)a.out_s)[i] = 0;
+    return;
+  }
   if (a.s_plain > 0) {
     ((uint32_t*)a.out_s)[i] = ((const uint32_t*)a.s)[i];
     return;
@@ -71,12 +82,16 @@ __global__ void repack_s_kernel(RepackArgs a) {
   else ((uint32_t*)a.out_s)[i] = ((const uint32_t*)a.s)[src];
 }
 
-// One thread per zero-point word: 8 columns of one (e, nb, g).
-__global__ void repack_z_kernel(RepackArgs a) {
+// One thread per zero-point word: 8 columns of one (e, nb, g); then zeros up to the region's end.
+__global__ void repack_z_kernel(RepackArgs a, int64_t padded) {
   const int nb_count = a.n >> 4;
   const int64_t total = (int64_t)a.experts * nb_count * a.groups * 2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
+  if (i >= padded) return;
+  if (i >= total) {
+    a.out_z[i] = 0u;
+    return;
+  }
   const int half = (int)(i & 1);
   int64_t rest = i >> 1;
   const int g = (int)(rest % a.groups);
@@ -96,11 +111,13 @@ void launch_repack(const RepackArgs& a, hipStream_t st) {
   const int64_t kun = a.w4 ? (a.k >> 5) : (a.k >> 4);
   const int64_t units = (int64_t)a.experts * (a.n >> 4) * kun * 16;
   hipLaunchKernelGGL(repack_w_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, a);
-  const int64_t ns = a.s_plain > 0 ? a.s_plain : (int64_t)a.experts * a.n * a.groups;
-  hipLaunchKernelGGL(repack_s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, a);
+  // (W regions are whole multiples of 256 bytes: n % 64 == 0 and k % 128 == 0)
+  const int64_t ns = a.s_plain > 0 ? padded_elems(a.s_plain, 4)
+                                   : padded_elems((int64_t)a.experts * a.n * a.groups, a.s_bytes);
+  hipLaunchKernelGGL(repack_s_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, a, ns);
   if (a.z) {
-    const int64_t nz = (int64_t)a.experts * (a.n >> 4) * a.groups * 2;
-    hipLaunchKernelGGL(repack_z_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, a);
+    const int64_t nz = padded_elems((int64_t)a.experts * (a.n >> 4) * a.groups * 2, 4);
+    hipLaunchKernelGGL(repack_z_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, a, nz);
   }
 }
 

@@ -368,3 +368,24 @@ def test_dense_streaming_split_needs_workspace():
         qg.gemm(p, x, None, y, 16, None)
     y = _run_dense(layer, acts, 16)
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
+
+
+@pytest.mark.parametrize("name", ["asym_g0_n320", "sym_g384", "fp8_block", "mxfp4_n192"])
+def test_prepare_writes_every_byte_of_the_image(name):
+    # regions whose sizes are not multiples of 256 bytes: the padding up to the next region
+    # must be written (zeros) whatever the buffer held before
+    layer = {
+        "asym_g0_n320": lambda: synth.dense_w4a16_asym_bf16(m=1, n=320, k=384, group=0, seed=1)[0],
+        "sym_g384": lambda: synth.dense_w4a16_sym_f16(m=1, n=192, k=1152, group=384, seed=2)[0],
+        "fp8_block": lambda: synth.moe_w8a8_fp8_block(t=1, experts=3, topk=1, n=256, k=384, seed=3)[0],
+        "mxfp4_n192": lambda: synth.moe_w4a16_mxfp4(t=1, experts=3, topk=1, n=192, k=128, seed=4)[0],
+    }[name]()
+    desc = layers.desc_for(layer)
+    buf = torch.full((qg.prepared_bytes(desc),), 0xAB, dtype=torch.uint8, device="cuda")
+    w, s = layers.to_dev(layer.w), layers.to_dev(layer.s)
+    z = None if layer.z is None else layers.to_dev(layer.z)
+    qg.prepare(desc, w, s, z, buf)
+    torch.cuda.synchronize()
+    ref = L.repack(layer)
+    got = buf.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} bytes differ"
