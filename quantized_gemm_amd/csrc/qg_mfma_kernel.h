@@ -637,11 +637,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT = false>
 static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // Two waves per SIMD throughout.  8 waves of BM x 32 for dense tiles, 256-row MoE blocks
-  // and every e4m3 tile; 16-bit 128-row MoE blocks keep 4 waves of 128 x 64 with two
-  // workgroups per CU (their blocks are many and short, and independent workgroups hide
-  // each other's barriers better: measured 15% faster there, while dense 128-row tiles
-  // gain ~10% from 8 waves).
-  constexpr int CW = (BM == 256 || !MOE || AF == A_FP8) ? 8 : 4;
+  // and every e4m3-weight tile; 128-row MoE blocks of the other weights (16-bit activations,
+  // and e2m1 under e4m3 activations) keep 4 waves of 128 x 64 with two workgroups per CU
+  // (their blocks are many and short, and independent workgroups hide each other's barriers
+  // better: measured 15% faster for 16-bit, 13-21% for e2m1 x e4m3, while dense 128-row
+  // tiles gain ~10% from 8 waves and 4-wave e4m3-weight tiles spill).
+  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8) ? 8 : 4;
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 
