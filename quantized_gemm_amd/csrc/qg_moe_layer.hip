@@ -12,7 +12,8 @@
 //    [0, E), float32 in slot order, one rounding at the end.
 //
 // All three are HBM-bound streams: 16-byte loads and stores, 8 elements per thread-piece,
-// consecutive lanes on consecutive pieces of a row.
+// consecutive lanes on consecutive pieces of a row.  The per-row e4m3 quantization reduces a
+// row's absmax within one wave for rows up to 2048 wide, within a workgroup beyond.
 #include "qg_device.h"
 #include "qg_kernels.h"
 
@@ -120,6 +121,53 @@ __global__ __launch_bounds__(256) void swiglu_e4m3_kernel(const uint16_t* __rest
   }
 }
 
+// Rows up to kSwigluWaveRow wide: one wave per row (four rows per workgroup), the absmax
+// reduced with wave shuffles only; every lane keeps up to four pieces in registers.
+constexpr int kSwigluWaveRow = 64 * 4 * 8;
+
+template <int IN>
+__global__ __launch_bounds__(256) void swiglu_e4m3_wave_kernel(const uint16_t* __restrict__ gu, int64_t rows,
+                                                               int64_t inter, uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;                       // whole waves leave together
+  const int64_t per_row = inter >> 3;
+  const uint16_t* row = gu + r * 2 * inter;
+  float act[4][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t c8 = lane + 64 * i;
+    if (c8 < per_row) {
+      swiglu8<IN>(row, inter, c8, act[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(act[i][e]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;     // correctly rounded division
+  if (lane == 0) scale[r] = sc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t c8 = lane + 64 * i;
+    if (c8 < per_row) {
+      u32x2 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(act[i][4 * h + e] / sc, -448.0f), 448.0f);
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+        o[h] = (uint32_t)v;
+      }
+      *(u32x2*)(codes + r * inter + 8 * c8) = o;
+    }
+  }
+}
+
 // One thread per 8 outputs of a token.
 template <int T>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
@@ -150,6 +198,14 @@ bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int ou
   const uint16_t* g = (const uint16_t*)gu;
   if (out_t == A_FP8) {
     if (inter > 256 * kSwigluE4m3Pieces * 8) return false;
+    if (inter <= kSwigluWaveRow) {
+      const dim3 grid((unsigned)((rows + 3) / 4));
+      if (in_t == O_BF16)
+        hipLaunchKernelGGL(swiglu_e4m3_wave_kernel<O_BF16>, grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out, out_scale);
+      else
+        hipLaunchKernelGGL(swiglu_e4m3_wave_kernel<O_F16>, grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out, out_scale);
+      return true;
+    }
     const dim3 grid((unsigned)rows);
     if (in_t == O_BF16) hipLaunchKernelGGL(swiglu_e4m3_kernel<O_BF16>, grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
     else hipLaunchKernelGGL(swiglu_e4m3_kernel<O_F16>, grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
