@@ -272,6 +272,18 @@ qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_
                         void* out, float* out_scale, void* stream);
 
 /*
+ * qg_quantize_e4m3_rows: per-token FP8 quantization of 16-bit activations, the input of the
+ * W4A8 and W8A8 products ("Humming" wiki article, "Reported performance": tokenwise FP8
+ * activations).  For each row r < rows of x (device [rows][k], in_type QG_A_F16 / QG_A_BF16):
+ *   scale[r] = max_i |x[r][i]| / 448 in float32 (1 for an all-zero row),
+ *   codes[r][i] = e4m3 code, round to nearest even, of clamp(x[r][i] / scale[r], -448, 448).
+ *   codes  device uint8 [rows][k] (8-byte aligned);  scale  device float32 [rows]
+ * k % 8 == 0 and k <= 8192, else QG_ERR_UNSUPPORTED.
+ */
+qg_status qg_quantize_e4m3_rows(const void* x, int64_t rows, int64_t k, int32_t in_type, uint8_t* codes, float* scale,
+                                void* stream);
+
+/*
  * qg_moe_combine: out[t][:] = sum over slots j with 0 <= topk_ids[t][j] < E of
  * weights[t][j] * y[t*topk + j][:], accumulated in float32 in slot order and rounded once
  * (nearest even).  Rows of other slots are never read.

@@ -5,7 +5,7 @@ stream supplies the hipStream_t, and every step of the computation runs in the
 library's HIP kernels.  The entry points mirror include/qg.h one to one:
 ``prepared_bytes``, ``prepare``, ``workspace_bytes``, ``gemm``, ``moe_block_m``,
 ``moe_capacity``, ``moe_align``, ``moe_grouped_map``, ``moe_gemm``, ``moe_swiglu``,
-``moe_combine``, ``dequant``, ``status_str``.
+``moe_combine``, ``quantize_e4m3_rows``, ``dequant``, ``status_str``.
 
 There is no fallback: if libqg.so is missing or cannot be loaded, every call raises.
 """
@@ -28,8 +28,8 @@ MOE_CONTIGUOUS, MOE_MASKED = 1, 2
 STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_ERR_ARCH_MISMATCH",
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
-           "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine", "qg_dequant", "qg_status_str",
-           "qg_version"]
+           "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine",
+           "qg_quantize_e4m3_rows", "qg_dequant", "qg_status_str", "qg_version"]
 
 
 class QGError(RuntimeError):
@@ -81,6 +81,8 @@ def lib():
         L.qg_moe_swiglu.argtypes, L.qg_moe_swiglu.restype = [vp, i64, i64, i32, i32, vp, vp, vp], i32
         L.qg_moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, i32, vp, vp]
         L.qg_moe_combine.restype = i32
+        L.qg_quantize_e4m3_rows.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.qg_quantize_e4m3_rows.restype = i32
         L.qg_dequant.argtypes, L.qg_dequant.restype = [pp, i32, vp, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
         L.qg_version.argtypes, L.qg_version.restype = [], i32
@@ -194,6 +196,12 @@ def moe_combine(y, weights, topk_ids, tokens: int, topk: int, num_experts: int, 
     st = lib().qg_moe_combine(_ptr(y), _ptr(weights), _ptr(topk_ids), tokens, topk, num_experts, n, dtype, _ptr(out),
                               _stream(stream))
     _check(st, "qg_moe_combine")
+
+
+def quantize_e4m3_rows(x, rows: int, k: int, in_type: int, codes, scale, stream=None):
+    """Per-token absmax e4m3 quantization of 16-bit rows: codes [rows][k] uint8, scale [rows] float32."""
+    st = lib().qg_quantize_e4m3_rows(_ptr(x), rows, k, in_type, _ptr(codes), _ptr(scale), _stream(stream))
+    _check(st, "qg_quantize_e4m3_rows")
 
 
 def dequant(p: Prepared, expert: int, out, stream=None):

@@ -642,6 +642,22 @@ qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_
   return launched();
 }
 
+qg_status qg_quantize_e4m3_rows(const void* x, int64_t rows, int64_t k, int32_t in_type, uint8_t* codes, float* scale,
+                                void* stream) {
+  if (rows < 0 || k <= 0) return QG_ERR_INVALID_ARG;
+  if (in_type != QG_A_F16 && in_type != QG_A_BF16) return QG_ERR_INVALID_ARG;
+  if (k % 8 != 0 || k > 8192) return QG_ERR_UNSUPPORTED;
+  if (rows > ((int64_t)1 << 31) - 1) return QG_ERR_UNSUPPORTED;
+  if (rows == 0) return QG_OK;
+  if (!x || !codes || !scale || !aligned16(x) || ((uintptr_t)codes & 7u) != 0 || ((uintptr_t)scale & 3u) != 0)
+    return QG_ERR_INVALID_ARG;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  if (!launch_quant_rows_e4m3(x, rows, k, in_type == QG_A_F16 ? O_F16 : O_BF16, codes, scale, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
 qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* topk_ids, int64_t tokens, int32_t topk,
                          int32_t num_experts, int64_t n, int32_t dtype, void* out, void* stream) {
   if (tokens < 0 || topk <= 0 || num_experts <= 0 || n <= 0) return QG_ERR_INVALID_ARG;

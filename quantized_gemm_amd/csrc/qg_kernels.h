@@ -76,6 +76,9 @@ void launch_dequant(const DequantArgs& a, hipStream_t st);
 // O_BF16; out_t: A_F16, A_BF16 or A_FP8 (then out_scale receives one scale per row).
 bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, float* out_scale,
                    hipStream_t st);
+// Per-row absmax e4m3 quantization of 16-bit rows (in_t O_F16 / O_BF16), k <= 8192, k % 8 == 0.
+bool launch_quant_rows_e4m3(const void* x, int64_t rows, int64_t k, int in_t, void* codes, float* scale,
+                            hipStream_t st);
 bool launch_combine(const void* y, const float* w, const int32_t* ids, int64_t tokens, int topk, int experts, int64_t n,
                     int dtype, void* out, hipStream_t st);
 

@@ -10,6 +10,8 @@
 //  * The down product is the grouped GEMM itself with one input row per slot.
 //  * Combine: out[t] = sum_j w[t, j] * y[t * topk + j] over the slots routed inside
 //    [0, E), float32 in slot order, one rounding at the end.
+//  * Per-token e4m3 quantization of 16-bit activations (the input of a W4A8 product), the
+//    same row quantizer without the SwiGLU.
 //
 // All three are HBM-bound streams: 16-byte loads and stores, 8 elements per thread-piece,
 // consecutive lanes on consecutive pieces of a row.  The per-row e4m3 quantization reduces a
@@ -73,21 +75,22 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
 // activations in registers while the row's absmax is reduced, then quantizes them.
 constexpr int kSwigluE4m3Pieces = 4;   // inter <= 256 * 4 * 8 = 8192
 
-template <int IN>
+template <int IN, bool SILU>
 __global__ __launch_bounds__(256) void swiglu_e4m3_kernel(const uint16_t* __restrict__ gu, int64_t inter,
                                                           uint8_t* __restrict__ codes, float* __restrict__ scale) {
   __shared__ float s_wmax[4];
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int64_t per_row = inter >> 3;
-  const uint16_t* row = gu + r * 2 * inter;
+  const uint16_t* row = gu + r * (SILU ? 2 : 1) * inter;
   float act[kSwigluE4m3Pieces][8];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kSwigluE4m3Pieces; ++i) {
     const int64_t c8 = tid + 256 * i;
     if (c8 < per_row) {
-      swiglu8<IN>(row, inter, c8, act[i]);
+      if constexpr (SILU) swiglu8<IN>(row, inter, c8, act[i]);
+      else unpack8<IN>(ldg16(row + 8 * c8), act[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(act[i][e]));
     }
@@ -125,7 +128,9 @@ __global__ __launch_bounds__(256) void swiglu_e4m3_kernel(const uint16_t* __rest
 // reduced with wave shuffles only; every lane keeps up to four pieces in registers.
 constexpr int kSwigluWaveRow = 64 * 4 * 8;
 
-template <int IN>
+// SILU: the row is [gate | up] and its SwiGLU is quantized; else the row itself (per-token
+// quantization of 16-bit activations).
+template <int IN, bool SILU>
 __global__ __launch_bounds__(256) void swiglu_e4m3_wave_kernel(const uint16_t* __restrict__ gu, int64_t rows,
                                                                int64_t inter, uint8_t* __restrict__ codes,
                                                                float* __restrict__ scale) {
@@ -133,14 +138,15 @@ __global__ __launch_bounds__(256) void swiglu_e4m3_wave_kernel(const uint16_t* _
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;                       // whole waves leave together
   const int64_t per_row = inter >> 3;
-  const uint16_t* row = gu + r * 2 * inter;
+  const uint16_t* row = gu + r * (SILU ? 2 : 1) * inter;
   float act[4][8];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t c8 = lane + 64 * i;
     if (c8 < per_row) {
-      swiglu8<IN>(row, inter, c8, act[i]);
+      if constexpr (SILU) swiglu8<IN>(row, inter, c8, act[i]);
+      else unpack8<IN>(ldg16(row + 8 * c8), act[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(act[i][e]));
     }
@@ -193,24 +199,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 }  // namespace
 
+template <bool SILU>
+static bool launch_rows_e4m3(const uint16_t* g, int64_t rows, int64_t inter, int in_t, void* out, float* out_scale,
+                             hipStream_t st) {
+  if (inter > 256 * kSwigluE4m3Pieces * 8) return false;
+  if (inter <= kSwigluWaveRow) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (in_t == O_BF16)
+      hipLaunchKernelGGL((swiglu_e4m3_wave_kernel<O_BF16, SILU>), grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out,
+                         out_scale);
+    else
+      hipLaunchKernelGGL((swiglu_e4m3_wave_kernel<O_F16, SILU>), grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out,
+                         out_scale);
+    return true;
+  }
+  const dim3 grid((unsigned)rows);
+  if (in_t == O_BF16)
+    hipLaunchKernelGGL((swiglu_e4m3_kernel<O_BF16, SILU>), grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
+  else
+    hipLaunchKernelGGL((swiglu_e4m3_kernel<O_F16, SILU>), grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
+  return true;
+}
+
 bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, float* out_scale,
                    hipStream_t st) {
   const uint16_t* g = (const uint16_t*)gu;
-  if (out_t == A_FP8) {
-    if (inter > 256 * kSwigluE4m3Pieces * 8) return false;
-    if (inter <= kSwigluWaveRow) {
-      const dim3 grid((unsigned)((rows + 3) / 4));
-      if (in_t == O_BF16)
-        hipLaunchKernelGGL(swiglu_e4m3_wave_kernel<O_BF16>, grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out, out_scale);
-      else
-        hipLaunchKernelGGL(swiglu_e4m3_wave_kernel<O_F16>, grid, dim3(256), 0, st, g, rows, inter, (uint8_t*)out, out_scale);
-      return true;
-    }
-    const dim3 grid((unsigned)rows);
-    if (in_t == O_BF16) hipLaunchKernelGGL(swiglu_e4m3_kernel<O_BF16>, grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
-    else hipLaunchKernelGGL(swiglu_e4m3_kernel<O_F16>, grid, dim3(256), 0, st, g, inter, (uint8_t*)out, out_scale);
-    return true;
-  }
+  if (out_t == A_FP8) return launch_rows_e4m3<true>(g, rows, inter, in_t, out, out_scale, st);
   const int64_t pieces = rows * (inter >> 3);
   const dim3 grid((unsigned)((pieces + 255) / 256));
   uint16_t* o = (uint16_t*)out;
@@ -220,6 +234,11 @@ bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int ou
   else if (in_t == O_F16 && out_t == A_F16) hipLaunchKernelGGL((swiglu_kernel<O_F16, O_F16>), grid, dim3(256), 0, st, g, rows, inter, o);
   else return false;
   return true;
+}
+
+bool launch_quant_rows_e4m3(const void* x, int64_t rows, int64_t k, int in_t, void* codes, float* scale,
+                            hipStream_t st) {
+  return launch_rows_e4m3<false>((const uint16_t*)x, rows, k, in_t, codes, scale, st);
 }
 
 bool launch_combine(const void* y, const float* w, const int32_t* ids, int64_t tokens, int topk, int experts, int64_t n,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     txt = open(os.path.join(ROOT, "include", "qg.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(qg_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(qg_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -186,3 +186,14 @@ def test_block_scaled_fp8_sizes_match_layout_reference():
                                    a_type=qg.A_FP8_E4M3)) == 0
     assert qg.prepared_bytes(_desc(w_type=qg.W_FP8_E4M3, s_type=qg.S_F32, group_k=128, has_zero=0,
                                    a_type=qg.A_FP8_E4M3, n=448)) == 0
+
+
+def test_quantize_rows_rejects_on_the_host():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.qg_quantize_e4m3_rows(fake, 0, 64, qg.A_BF16, fake, fake, None) == 0         # no rows: no-op
+    assert lib.qg_quantize_e4m3_rows(fake, 4, 64, qg.A_FP8_E4M3, fake, fake, None) == 1     # input must be 16-bit
+    assert lib.qg_quantize_e4m3_rows(fake, 4, 60, qg.A_BF16, fake, fake, None) == 2
+    assert lib.qg_quantize_e4m3_rows(fake, 4, 8200, qg.A_BF16, fake, fake, None) == 2
+    assert lib.qg_quantize_e4m3_rows(fake, 4, 64, qg.A_BF16, None, fake, None) == 1
+    assert lib.qg_quantize_e4m3_rows(ctypes.c_void_p(4100), 4, 64, qg.A_BF16, fake, fake, None) == 1

@@ -270,3 +270,26 @@ def test_moe_layer_mxfp4(t):
     got = run_layer_mxfp4(up, down, acts)
     ref = ML.moe_layer_reference(up, down, acts, acts.topk_weights)
     assert R.relative_error(got, ref) <= TOL16
+
+
+# ---- per-token e4m3 quantization of 16-bit activations -------------------------------------
+
+@pytest.mark.parametrize("rows,k,dtype", [(1, 8, "bf16"), (37, 1408, "bf16"), (5, 2048, "f16"), (9, 4096, "bf16"),
+                                          (3, 7168, "bf16"), (4, 8192, "f16")])
+def test_quantize_e4m3_rows_is_bit_exact(rows, k, dtype):
+    # the inputs are exact in float32, and both sides take every decision in float32 with
+    # correctly rounded divisions and round-to-nearest-even: codes and scales must agree bit for bit
+    from oracle import quant as Q
+    bits, _ = synth.act_rows(rows, k, dtype, sigma=3.0, seed=rows + k)
+    bits = bits.copy()
+    if rows > 2:
+        bits[1] = 0                                         # an all-zero row: scale 1, codes 0
+        bits[2, :4] = (synth.f32_to_bf16_bits if dtype == "bf16" else synth.f32_to_f16_bits)(
+            np.array([1e4, -3e-3, 6e-5, -6e-5], np.float32))
+    codes = torch.full((rows, k), 0x7F, dtype=torch.uint8, device="cuda")
+    scale = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    qg.quantize_e4m3_rows(_dev16(bits), rows, k, Q_ACT[dtype], codes, scale)
+    torch.cuda.synchronize()
+    rc, rs = Q.absmax_rows(F.decode_act(bits, dtype).astype(np.float32))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), rc), f"{np.count_nonzero(codes.cpu().numpy() != rc)} codes differ"
