@@ -143,17 +143,20 @@ LAYERS = {
                             desc="MoE layer MXFP4 W4A16, E=128 top-8, hidden 7168, intermediate 2048: "
                                  "align + gate/up + SwiGLU + down + combine"),
     "moe_w4a8_mxfp4": dict(down="moe_down_w4a8_mxfp4", hidden=7168, inter=2048, act="e4m3",
-                           desc="MoE layer W4A8 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: align + gate/up + "
+                           desc="MoE layer W4A8 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: per-token e4m3 "
+                                "quantization of bf16 hidden states + align + gate/up + "
                                 "SwiGLU with per-row e4m3 quantization + down + combine"),
     "moe_w4a8_int4": dict(down="moe_down_w4a8", hidden=4096, inter=1408, act="e4m3",
-                          desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: "
-                               "align + gate/up + SwiGLU with per-row e4m3 quantization + down + combine"),
+                          desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: per-token "
+                               "e4m3 quantization of bf16 hidden states + align + gate/up + SwiGLU with per-row e4m3 "
+                               "quantization + down + combine"),
 }
 
 
 def bench_moe_layer(args, wl):
-    """Whole MoE layers: align -> gate/up product -> SwiGLU -> down product (one row per slot)
-    -> routing-weighted combine, each step timed with HIP events on the launch stream."""
+    """Whole MoE layers: (FP8-activation layers: per-token e4m3 quantization of bf16 hidden
+    states) -> align -> gate/up product -> SwiGLU -> down product (one row per slot) ->
+    routing-weighted combine, each step timed with HIP events on the launch stream."""
     import torch
     import quantized_gemm_amd as qg
     from quantized_gemm_amd import layers, synth
@@ -177,6 +180,12 @@ def bench_moe_layer(args, wl):
         keep += [b1, b2]
         hs.append((h1, h2))
     x_all, xs_all = layers.acts_to_dev(acts)
+    # FP8-activation layers start from bf16 hidden states, quantized per token on the GPU
+    # (timed as the layer's first step)
+    q_in = up.a_type == "e4m3"
+    if q_in:
+        h_bits, _ = synth.act_rows(tmax, up.k, "bf16", sigma=1.0, seed=7)
+        h_all = layers.to_dev(h_bits)
     ids_all = torch.from_numpy(np.ascontiguousarray(acts.topk_ids)).cuda()
     w_all = torch.from_numpy(np.ascontiguousarray(acts.topk_weights)).cuda()
     a_e4m3 = lw["act"] == "e4m3"
@@ -198,7 +207,7 @@ def bench_moe_layer(args, wl):
             ws1=torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda"),
             ws2=torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda"))
     stream = torch.cuda.current_stream()
-    names = ["align", "gate_up", "swiglu", "down", "combine"]
+    names = (["quant"] if q_in else []) + ["align", "gate_up", "swiglu", "down", "combine"]
     call = [0]
 
     def one_step(ev=None):
@@ -208,24 +217,35 @@ def bench_moe_layer(args, wl):
             d = st[t]
             rows = t * topk
             xs = None if xs_all is None else xs_all[:t]
-            mark = (lambda j: ev[i][j].record(stream)) if ev is not None else (lambda j: None)
-            mark(0)
+            nxt = [0]
+
+            def mark():
+                if ev is not None:
+                    ev[i][nxt[0]].record(stream)
+                nxt[0] += 1
+
+            mark()
+            x = x_all[:t]
+            if q_in:
+                qg.quantize_e4m3_rows(h_all[:t], t, up.k, qg.A_BF16, x, xs)
+                mark()
             qg.moe_align(d["ids"], t, topk, experts, d["bm"], d["sid"], d["eid"], d["npp"])
-            mark(1)
-            qg.moe_gemm(h1, x_all[:t], xs, d["sid"], d["eid"], d["npp"], t, topk, d["bm"], d["y1"], d["ws1"])
-            mark(2)
+            mark()
+            qg.moe_gemm(h1, x, xs, d["sid"], d["eid"], d["npp"], t, topk, d["bm"], d["y1"], d["ws1"])
+            mark()
             qg.moe_swiglu(d["y1"], rows, lw["inter"], qg.O_BF16, qg.A_FP8_E4M3 if a_e4m3 else qg.A_BF16, d["act"],
                           d["asc"])
-            mark(3)
+            mark()
             qg.moe_gemm(h2, d["act"], d["asc"], d["sid"], d["eid"], d["npp"], rows, 1, d["bm"], d["y2"], d["ws2"])
-            mark(4)
+            mark()
             qg.moe_combine(d["y2"], d["w"], d["ids"], t, topk, experts, lw["hidden"], qg.O_BF16, d["out"])
-            mark(5)
+            mark()
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in wl["sweep"]] for _ in range(args.steps)]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in wl["sweep"]]
+          for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
