@@ -76,6 +76,15 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   __shared__ __attribute__((aligned(16))) uint8_t sS[NCB * KQ * RCR * SB];
   __shared__ __attribute__((aligned(8))) uint32_t sZ[NCB * KQ * RCR * 2];
   __shared__ int sRowTok[BM];     // activation row of each tile row (-1: none)
+  // int4 / uint4 with 16-bit activations: the magic-number operand needs each 128-wide chunk's
+  // activation row sums; they are the same for every column block, so for tiles of 16 rows and
+  // more the workgroup adds them once per round in LDS (slot = part * RCR + chunk, then row)
+  // instead of an all-ones MFMA per chunk in every wave (measured: 16 rows -6%, 64 rows -2%;
+  // 4-row tiles, one round of a few chunks, are faster with the MFMA)
+  constexpr bool RSUM = (WP == WP_INT4_MAGIC || WP == WP_INT4Q_MAGIC) && AF != A_FP8 && MT != 0;
+  constexpr int NRS = RSUM ? KQ * RCR * BM : 4;
+  static_assert(!RSUM || 2 * NRS <= NTHR, "two threads per row sum");
+  __shared__ __attribute__((aligned(16))) float sR[NRS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,6 +248,29 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
         store_stage(st);
         __syncthreads();
         if (rnd + 1 < r1) load_stage(rnd + 1, st);     // next round in flight during this one
+        if constexpr (RSUM) {
+          // thread pair (2s, 2s+1) adds the two halves of row sum s (64 values each); rows
+          // without a token and chunks past the end were staged as zeros
+          if (tid < 2 * NRS) {
+            const int sidx = tid >> 1, h = tid & 1;
+            const int row = sidx % BM, slot = sidx / BM;
+            const int pq = slot / RCR, pc = slot - pq * RCR;
+            const uint8_t* src = sA + row * AROW + pq * PART + pc * 256 + h * 128;
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              const u32x4 w = *(const u32x4*)(src + 16 * v);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (AF == A_F16) sum += f16_bits_to_f32(w[e] & 0xFFFFu) + f16_bits_to_f32(w[e] >> 16);
+                else sum += bf16_bits_to_f32(w[e] & 0xFFFFu) + bf16_bits_to_f32(w[e] >> 16);
+              }
+            }
+            sum += __shfl_xor(sum, 1, 64);
+            if (h == 0) sR[slot * BM + row] = sum;
+          }
+          __syncthreads();
+        }
 #pragma unroll
         for (int lc = 0; lc < RCR; ++lc) {
           const int c = rr * RCR + lc;                  // chunk of the batch (compile-time)
@@ -320,9 +352,17 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                     if constexpr (QUAD) av = a16_to_quad(av);
                   }
                   if (!aok) av = u32x4{0u, 0u, 0u, 0u};
-                  R[mt] = mfma16x16x32<MAF>(av, ones, R[mt]);
+                  if constexpr (!RSUM) R[mt] = mfma16x16x32<MAF>(av, ones, R[mt]);
                   P[mt] = mfma16x16x32<MAF>(av, b, P[mt]);
                 }
+              }
+              if constexpr (RSUM) {
+                // rows 16mt + 4g .. + 3 of the lane's accumulator
+                const int rslot = q * RCR + lc;
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+                  R[mt] = (16 * mt + 4 * g + 3 < BM) ? *(const f32x4*)&sR[rslot * BM + 16 * mt + 4 * g]
+                                                     : f32x4{0.f, 0.f, 0.f, 0.f};
               }
               const uint32_t sbits = ((const uint16_t*)sS)[slot * 16 + r];
               const float sp = (ST == S_F16 ? f16_bits_to_f32(sbits) : bf16_bits_to_f32(sbits)) *
