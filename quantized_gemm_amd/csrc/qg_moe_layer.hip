@@ -174,25 +174,39 @@ __global__ __launch_bounds__(256) void swiglu_e4m3_wave_kernel(const uint16_t* _
   }
 }
 
-// One thread per 8 outputs of a token.
+// One thread per 8 outputs of a token.  Slots go in groups of 8 with every row load of a
+// group in flight at once: a dropped slot's row exists (it is only unwritten), so it is read
+// like the others and discarded with a select, never multiplied (it may hold NaN).
 template <int T>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
                                                       const int32_t* __restrict__ ids, int64_t tokens, int topk,
                                                       int experts, int64_t n, uint16_t* __restrict__ out) {
+  constexpr int G = 8;
   const int64_t per_row = n >> 3;
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= tokens * per_row) return;
   const int64_t t = p / per_row, c8 = p - t * per_row;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int64_t f = t * topk + j;
-    const int e = ids[f];
-    if (e < 0 || e >= experts) continue;       // dropped slot: its row was never written
-    const float wj = w[f];
-    float v[8];
-    unpack8<T>(ldg16(y + f * n + 8 * c8), v);
+  for (int j0 = 0; j0 < topk; j0 += G) {
+    u32x4 v[G];
+    bool ok[G];
+    float wj[G];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u;
+      const int64_t f = t * topk + (j < topk ? j : topk - 1);
+      const int e = ids[f];
+      ok[u] = j < topk && e >= 0 && e < experts;
+      wj[u] = w[f];
+      v[u] = ldg16(y + f * n + 8 * c8);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      float vv[8];
+      unpack8<T>(v[u], vv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = ok[u] ? __builtin_fmaf(wj[u], vv[i], acc[i]) : acc[i];
+    }
   }
   *(u32x4*)(out + t * n + 8 * c8) = pack8<T>(acc);
 }
