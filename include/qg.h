@@ -286,7 +286,8 @@ qg_status qg_quantize_e4m3_rows(const void* x, int64_t rows, int64_t k, int32_t 
 /*
  * qg_moe_combine: out[t][:] = sum over slots j with 0 <= topk_ids[t][j] < E of
  * weights[t][j] * y[t*topk + j][:], accumulated in float32 in slot order and rounded once
- * (nearest even).  Rows of other slots are never read.
+ * (nearest even).  Rows of other slots may be read but never contribute (they may hold
+ * anything, NaN included).
  *   y         device [T*topk][n] of dtype (QG_O_F16 / QG_O_BF16), e.g. the down product's output
  *   weights   device float32 [T][topk] (the router's probabilities; applied as given)
  *   topk_ids  device int32 [T][topk]
