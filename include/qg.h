@@ -85,7 +85,11 @@ enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                 
  *   int4 weights, QG_C_W_TO_FP8, bf16|f16 scales (group a multiple of 128, or 0 =
  *       per channel), e4m3 activations                                 [W4A8]
  *   e2m1 weights, UE8M0 scales, group_k == 32, f16|bf16 activations  [MXFP4 W4A16]
+ *   e2m1 weights, UE8M0 scales, group_k == 32, e4m3 activations      [MXFP4 W4A8]
  *   e4m3 weights, f32 channel scales (group_k == 0), e4m3 activations [W8A8]
+ *   e4m3 weights, f32 block scales (group_k == 128: one scale per 128 output channels x
+ *       128 K, scales [E][N/128][K/128], n % 128 == 0), e4m3 activations with one f32
+ *       scale per (row, 128-wide K group)                              [block-scaled W8A8]
  */
 typedef struct {
   int32_t w_type;       /* QG_W_*                                                      */
@@ -134,8 +138,10 @@ size_t qg_prepared_bytes(const qg_layer_desc* desc);
  *            int4/uint4  uint32 [E][N][K/8]  (element k at bits 4*(k%8), low nibble first)
  *            e2m1        uint8  [E][N][K/2]  (even k in the low nibble)
  *            e4m3        uint8  [E][N][K]
- *   scales device, [E][N][G] of the scale type (G = K/group_k, or 1 per channel)
+ *   scales device, [E][N][G] of the scale type (G = K/group_k, or 1 per channel);
+ *          block-scaled e4m3: float32 [E][N/128][K/128]
  *   zeros  device, uint8 [E][N][G] holding 0..15 when has_zero, else NULL
+ *   Every byte of the prepared image is written (alignment padding as zeros).
  *   dev_out device buffer of at least qg_prepared_bytes(desc) bytes (must not
  *          overlap the inputs); `out` (host) receives the handle.
  * Enqueued on `stream`; the inputs may be freed once the stream has passed it.
@@ -159,7 +165,8 @@ size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t top
 /*
  * qg_gemm: dense Y[m, n] = sum_k X[m, k] * W[n, k] for a prepared dense layer.
  *   x        device [M][K] of a_type (f16/bf16 values or e4m3 codes)
- *   x_scale  device float32 [M] per-token scales for e4m3 activations, else NULL
+ *   x_scale  device float32 per-token scales for e4m3 activations, else NULL: [M], or
+ *            [M][K/128] for block-scaled layers
  *   y        device [M][N] of out_type, written in full (fp32 accumulation, RNE)
  *   ws       device workspace of ws_bytes >= qg_workspace_bytes(p, m, 0)
  * The tile / split-K choice is made from M on the host (the M-bucket selector).
@@ -227,7 +234,8 @@ qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, i
 /*
  * qg_moe_gemm: grouped GEMM over the aligned rows.  For every (token t, slot j)
  * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
- *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3, else NULL
+ *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3 ([T][K/128] for
+ *            block-scaled layers), else NULL
  *   sorted_ids / expert_ids / num_post_pad  from qg_moe_align with the same block_m
  *   block_m  4, 16, 32 or 64 (weight-streaming kernel) or 128, 256 (MFMA kernel; 256 not
  *            for e4m3 or int4->e4m3 weights); qg_moe_block_m picks one, any other is
@@ -302,6 +310,7 @@ qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* top
  * [N][K] = code value (minus zero point) times scale, read through the same
  * unpack routines the GEMM kernels use.  Every such value is exact in float32
  * except e4m3 x f32 channel scale, which is one correctly rounded product.
+ * Block-scaled e4m3 layers: QG_ERR_UNSUPPORTED (their image is checked byte for byte).
  * For checking the prepared layout; not on the GEMM path.
  */
 qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* stream);
