@@ -206,7 +206,7 @@ constexpr int kCUs = 256;
 constexpr int64_t kStreamMaxRows = 64;
 
 // The int4 -> e4m3 kernel uses 128-row tiles only.
-bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8; }
+bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8 && pi.wp_mfma != WP_FP8_BLOCK; }
 
 // Split K over workgroups when 128-row tiles would fill at most half of the CUs (above
 // that, writing and re-reading the fp32 partials costs more than the idle CUs):
@@ -282,9 +282,9 @@ int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
   return sp;
 }
 
-// Block-scaled e4m3: one kernel (128 x 256 tiles, a promotion per 128-wide step) for every
-// row count; dense grids with at most half a workgroup per CU split K over up to 8
-// workgroups (whole steps, at least two per slice), the batch-invariant flag excepted.
+// Block-scaled e4m3 above the streaming sizes (and at every size under the batch-invariant
+// flag): 128 x 256 tiles with a promotion per 128-wide step; dense grids with at most half a
+// workgroup per CU split K over up to 8 workgroups (whole steps, at least two per slice).
 bool is_block(const PathInfo& pi) { return pi.wp_small == WP_FP8_BLOCK; }
 MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
   MfmaTile t{};
@@ -302,7 +302,7 @@ MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
 
 // Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
-  if (is_block(pi)) {
+  if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
   }
@@ -422,7 +422,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   fill_stream_args(a, p);
   a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
-  if (is_block(pi)) {
+  if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     if (t.ksplit > 1) {
       const size_t need = dense_workspace(p, pi, m);
@@ -482,7 +482,9 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
          (long long)p->desc.k, t.mt, t.grid_x, t.grid_y, sp);
   if (!launch_stream_gemm(a, t, pi.wp_small, pi.af, pi.of, pi.st, p->desc.has_zero != 0, false, (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
-  if (sp > 1 && !launch_split_reduce(a, pi.wp_small == WP_FP8, pi.af == A_FP8, pi.of, (hipStream_t)stream))
+  // block-scaled partials are scaled already; the others take their scales in the reduction
+  if (sp > 1 && !launch_split_reduce(a, pi.wp_small == WP_FP8, pi.af == A_FP8 && !is_block(pi), pi.of,
+                                     (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();
 }
@@ -498,7 +500,6 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   // which costs more than the occasional second pass over an expert's weights).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
-  if (is_block(pi)) return 128;                  // the block-scaled kernel's only tile
   if (pi.binv) return (mean < 512 || !mfma_rows256(pi)) ? 128 : 256;   // MFMA blocks at every size
   if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
@@ -576,7 +577,6 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
     return QG_ERR_UNSUPPORTED;
   if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (pi.binv && block_m <= kStreamMaxRows) return QG_ERR_UNSUPPORTED;   // one MMA type for every size
-  if (is_block(pi) && block_m != 128) return QG_ERR_UNSUPPORTED;
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;

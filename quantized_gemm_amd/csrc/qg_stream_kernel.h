@@ -19,6 +19,8 @@
 //  * e4m3 x e4m3: fp8 MFMA, per-token x per-channel scale in the epilogue.
 //  * e4m3 x e2m1 (W4A8 MXFP4): the e2m1 codes and their UE8M0 block scales go to the
 //    scaled fp8/fp4 MFMA as they are; per-token scale in the epilogue.
+//  * block-scaled e4m3: one fp8 MFMA per chunk (= one 128-wide scale group) from zero,
+//    promoted by the row's activation scale times the weight block's scale.
 //
 // Work split inside a workgroup of NCB x KQ waves: wave (cb, q) owns 16-column block cb
 // and the q-th contiguous part of K.  Activations, scales and zero points for all parts
@@ -36,16 +38,16 @@ namespace qg {
 
 template <int WP, int AF>
 struct StreamTraits {
-  static constexpr bool kFp8Mfma = (WP == WP_FP8);
+  static constexpr bool kFp8Mfma = (WP == WP_FP8 || WP == WP_FP8_BLOCK);
   static constexpr int ABYTES = (AF == A_FP8) ? 1 : 2;
   static constexpr int B_U4 = kFp8Mfma ? 2 : 1;       // 16-byte weight units per lane per chunk
   // staged scale bytes per (column block, chunk): int4 paths 16 scales, fp4 4 groups x 16 bytes
-  static constexpr int SBYTES = (WP == WP_FP8) ? 0 : (WP == WP_FP4 ? 64 : 32);
+  static constexpr int SBYTES = kFp8Mfma ? 0 : (WP == WP_FP4 ? 64 : 32);
 };
 
 // Chunks per wave whose weights are in flight at once (<= 16 KB per wave).
 template <int WP>
-constexpr int stream_max_chunks() { return WP == WP_FP8 ? 8 : 16; }
+constexpr int stream_max_chunks() { return (WP == WP_FP8 || WP == WP_FP8_BLOCK) ? 8 : 16; }
 
 // Chunks per K part staged per round: <= 64 KB of activations in LDS.
 template <int WP, int AF, int MT, int KQ>
@@ -85,6 +87,13 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   constexpr int NRS = RSUM ? KQ * RCR * BM : 4;
   static_assert(!RSUM || 2 * NRS <= NTHR, "two threads per row sum");
   __shared__ __attribute__((aligned(16))) float sR[NRS];
+  // block-scaled e4m3: each 128-wide chunk is one scale group; its product is promoted by the
+  // row's activation scale (staged per round, slot = part * RCR + chunk, then row) times the
+  // 128-column weight block's scale (loaded with the chunk's weights)
+  constexpr bool BLOCK = (WP == WP_FP8_BLOCK);
+  constexpr int NSA = BLOCK ? KQ * RCR * BM : 4;
+  static_assert(!BLOCK || NSA <= NTHR, "one thread per staged row scale");
+  __shared__ __attribute__((aligned(16))) float sSA[NSA];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,6 +158,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     u32x4 a[AP_PER_T];
     u32x4 s;
     u32x2 z;
+    float sa;
   };
   auto load_stage = [&](int rnd, Stage& st) {
 #pragma unroll
@@ -164,6 +174,15 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
       const bool ok = p < APIECES && tok >= 0 && chunk_in_part < pn;
       const int64_t off = (int64_t)tok * xrow_bytes + (int64_t)(cbase + pq * per + rnd * RCR) * 128 * T::ABYTES + 16 * pc;
       st.a[i] = bload16(xr, ok ? (int)off : kOOB);
+    }
+    if constexpr (BLOCK) {
+      const int slot = tid / BM, row = tid - slot * BM;             // slot = part * RCR + chunk
+      const int spq = slot / RCR, sc = slot - spq * RCR;
+      const int chunk_in_part = rnd * RCR + sc;
+      const int pn = max(0, min(nchunks, spq * per + per) - spq * per);
+      const int tok = sRowTok[min(row, BM - 1)];
+      const bool ok = tid < NSA && tok >= 0 && chunk_in_part < pn;
+      st.sa = ok ? a.x_scale[(int64_t)tok * (a.k >> 7) + cbase + spq * per + chunk_in_part] : 0.f;
     }
     if constexpr (T::SBYTES > 0) {
       const int slot = tid / SPPC, sq = tid - slot * SPPC;          // slot = (cb, part, chunk)
@@ -203,6 +222,9 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
         *(u32x4*)(sA + row * AROW + 16 * cp) = st.a[i];
       }
     }
+    if constexpr (BLOCK) {
+      if (tid < NSA) sSA[tid] = st.sa;
+    }
     if constexpr (T::SBYTES > 0) {
       if (tid < SPIECES) *(u32x4*)(sS + 16 * tid) = st.s;
       if constexpr (ZERO) {
@@ -229,6 +251,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     Stage st;
     load_stage(r0, st);
     u32x4 bw[CHMAX][T::B_U4];
+    float swb[BLOCK ? CHMAX : 1];          // block-scaled: the weight block's scale per chunk
 #pragma unroll
     for (int c = 0; c < CHMAX; ++c) {
       const int ch = cbase + my0 + b0 + c;
@@ -237,6 +260,10 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
         const int64_t ku = T::kFp8Mfma ? ((int64_t)ch * 8 + 2 * g + u) : ((int64_t)ch * 4 + g);
         const bool ok = (b0 + c) < myn && wact;
         bw[c][u] = bload16_stream(wr, ok ? (int)((((int64_t)nbw * kun + ku) * 16 + r) << 4) : kOOB);
+      }
+      if constexpr (BLOCK) {
+        const bool ok = (b0 + c) < myn && wact;
+        swb[c] = ok ? ((const float*)a.s)[((int64_t)expert * (a.n >> 7) + (nbw >> 3)) * (a.k >> 7) + ch] : 0.f;
       }
     }
 
@@ -277,7 +304,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
           if ((b0 + c) >= myn || !wact) continue;
             const uint8_t* arow0 = sA + q * PART + lc * 128 * T::ABYTES;
             const int slot = (cb * KQ + q) * RCR + lc;
-            if constexpr (WP == WP_FP8) {
+            if constexpr (WP == WP_FP8 || WP == WP_FP8_BLOCK) {
     #pragma unroll
               for (int mt = 0; mt < NMT; ++mt) {
                 const uint8_t* ap = arow0 + (16 * mt + ar) * AROW + 32 * g;
@@ -288,7 +315,17 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                   A[i] = aok ? (int)a0[i] : 0; A[4 + i] = aok ? (int)a1[i] : 0;
                   B[i] = (int)bw[c][0][i]; B[4 + i] = (int)bw[c][1][i];
                 }
-                acc[mt] = mfma16x16x128_fp8(A, B, acc[mt]);
+                if constexpr (BLOCK) {
+                  // rows 16mt + 4g .. + 3 of the lane's accumulator (4-row tiles: lanes g > 0
+                  // hold the zero rows 4..15)
+                  const f32x4 P = mfma16x16x128_fp8(A, B, f32x4{0.f, 0.f, 0.f, 0.f});
+                  const int rs = (q * RCR + lc) * BM + 16 * mt + 4 * g;
+                  const f32x4 sa4 = (16 * mt + 4 * g + 3 < BM) ? *(const f32x4*)&sSA[rs] : f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(sa4[i] * swb[c], P[i], acc[mt][i]);
+                } else {
+                  acc[mt] = mfma16x16x128_fp8(A, B, acc[mt]);
+                }
               }
             } else if constexpr (WP == WP_FP4 && AF == A_FP8) {
               // e4m3 activations x e2m1 weights, natively: the lane's 16-byte unit is the
@@ -412,7 +449,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
       continue;
     }
     if constexpr (WP == WP_FP8) v *= ((const float*)a.s)[(int64_t)expert * a.n + n];
-    if constexpr (AF == A_FP8) v *= a.x_scale[tok];
+    if constexpr (AF == A_FP8 && !BLOCK) v *= a.x_scale[tok];
     int64_t orow;
     if constexpr (MOE) orow = a.sorted_ids[rowbase + row];
     else orow = rowbase + row;
@@ -445,7 +482,7 @@ static bool launch_shape(const StreamArgs& a, const StreamTile& t, hipStream_t s
 
 template <int WP, int AF, int OF, int ST, bool ZERO, bool MOE>
 static bool launch_mt(const StreamArgs& a, const StreamTile& t, hipStream_t st) {
-  if constexpr (WP == WP_FP8) {
+  if constexpr (WP == WP_FP8 || WP == WP_FP8_BLOCK) {
     if (t.ncb == 1 && t.kq == 8) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 1, 8>(a, t, st);
     if constexpr (!MOE)
       if (t.ncb == 8 && t.kq == 1) return launch_shape<WP, AF, OF, ST, ZERO, MOE, 8, 1>(a, t, st);

@@ -1,8 +1,10 @@
 """GPU parity of block-scaled W8A8 (e4m3 weights with 128 x 128 block scales, e4m3
 activations with one scale per (row, 128-wide K group)), through the C ABI.
 
-Bars: prepared bytes bit-exact; products max|Y - Y_ref| / max|Y_ref| <= 2e-2 (e4m3
-activations); with the batch-invariant flag, rows bitwise independent of M.
+Both kernel families: the streaming kernel up to 64 rows (and MoE blocks up to 64), the
+block-scaled MFMA kernel above.  Bars: prepared bytes bit-exact; products
+max|Y - Y_ref| / max|Y_ref| <= 2e-2 (e4m3 activations); with the batch-invariant flag, rows
+bitwise independent of M.
 """
 import numpy as np
 import pytest
@@ -44,7 +46,8 @@ def _dense(layer, acts, m, flags=0):
 @pytest.mark.parametrize("m,n,k", [(1, 384, 1152), (5, 384, 1152), (64, 512, 2048), (100, 512, 2048),
                                    (129, 384, 1152), (600, 768, 1024), (1, 1024, 4096)])
 def test_dense(m, n, k):
-    # (1, 384, 1152): 9 steps, no split; (64, 512, 2048): 2 tiles, K split 8 ways; (1, 1024, 4096): split
+    # 1..64 rows: the streaming kernel (4-row tiles; 16..64-row tiles with K split over
+    # workgroups); above: the block-scaled MFMA kernel, split over K when its tiles are few
     layer, acts = synth.dense_w8a8_fp8_block(m=m, n=n, k=k, seed=m + n)
     y = layers.out_bits_to_f64(_dense(layer, acts, m))
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
@@ -65,12 +68,12 @@ def test_batch_invariant_rows():
         assert np.array_equal(got, ref[:m]), f"M={m}"
 
 
-@pytest.mark.parametrize("t", [1, 30, 300])
+@pytest.mark.parametrize("t", [1, 30, 60, 300])
 def test_moe(t):
     layer, acts = synth.moe_w8a8_fp8_block(t=t, experts=4, topk=2, n=256, k=512, seed=t)
     p, buf = layers.prepare_layer(layer)
     bm = qg.moe_block_m(p, t, 2)
-    assert bm == 128
+    assert bm in (4, 16, 32, 64, 128)          # streaming blocks for few rows per expert, else 128
     cs, cb = qg.moe_capacity(t, 2, 4, bm)
     s = torch.empty(cs, dtype=torch.int32, device="cuda")
     e = torch.empty(cb, dtype=torch.int32, device="cuda")
