@@ -5,8 +5,9 @@
 // block exponents cannot carry them: each 128-wide K step is one 16x16x128 fp8 MFMA per
 // tile, computed from zero and promoted into the float32 accumulator,
 //     acc += (sa[row, step] * sw[n / 128, step]) * P.
-// Tile: 128 rows x 256 columns, 4 waves owning 64 columns each (one 128-column scale block
-// per wave, so sw is one value per wave and step); activations staged through LDS
+// Tile: 128 rows x 256 columns, 8 waves owning 32 columns each (inside one 128-column scale
+// block, so sw is one value per wave and step; two waves per SIMD, so one wave's promotion
+// arithmetic overlaps the other's matrix products); activations staged through LDS
 // (double-buffered, 128-byte row segment per step, XOR swizzle by row bits 1..3), the
 // step's 128 row scales staged beside them; weights HBM -> VGPR two steps ahead.  Dense
 // shapes with few tiles split K over workgroups (grid z) into fp32 partials that are
@@ -16,14 +17,16 @@
 
 namespace qg {
 
-template <int OF, bool MOE, bool SPLIT>
-__global__ __launch_bounds__(256) void mfma_fp8_block_kernel(MfmaArgs a) {
+template <int OF, bool MOE, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW) void mfma_fp8_block_kernel(MfmaArgs a) {
   constexpr int BM = 128, BN = 256;
+  constexpr int NTHR = 64 * NW;             // NW waves, each owning BN / NW columns
   constexpr int ROWB = 128;                 // one 128-k step of e4m3 activations
   constexpr int STAGE = BM * ROWB;
-  constexpr int APT = STAGE / 16 / 256;
+  constexpr int APT = STAGE / 16 / NTHR;
   constexpr int MT = BM / 16;               // 16-row MFMA tiles
-  constexpr int NT = 4;                     // 16-column MFMA tiles per wave
+  constexpr int WCOL = BN / NW;
+  constexpr int NT = WCOL / 16;             // 16-column MFMA tiles per wave
 
   __shared__ __attribute__((aligned(16))) uint8_t sA[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float sSA[2][BM];
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void mfma_fp8_block_kernel(MfmaArgs a) {
       rowbase = (int64_t)(id - ntile * mtiles) * BM;
     }
   }
-  for (int i = tid; i < BM; i += 256) {
+  for (int i = tid; i < BM; i += NTHR) {
     const int64_t rr = rowbase + i;
     int tok;
     if constexpr (MOE) {
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void mfma_fp8_block_kernel(MfmaArgs a) {
   }
   __syncthreads();
 
-  const int64_t col0 = (int64_t)ntile * BN + 64 * wave;     // this wave's first column
+  const int64_t col0 = (int64_t)ntile * BN + WCOL * wave;   // this wave's first column
   const int ngroups = a.k >> 7;                              // 128-wide K groups = steps
   const int nsteps = SPLIT ? ngroups / a.ksplit : ngroups;
   const int kstep0 = SPLIT ? (int)blockIdx.z * nsteps : 0;
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void mfma_fp8_block_kernel(MfmaArgs a) {
   int a_off[APT];
 #pragma unroll
   for (int i = 0; i < APT; ++i) {
-    const int p = tid + 256 * i;
+    const int p = tid + NTHR * i;
     const int row = p >> 3, pc = p & 7;
     const int lc = pc ^ ((row >> 1) & 7);
     const int tok = sRowTok[row];
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void mfma_fp8_block_kernel(MfmaArgs a) {
   };
   auto store_a = [&](int buf, const u32x4* src, float sa) {
 #pragma unroll
-    for (int i = 0; i < APT; ++i) *(u32x4*)(sA + buf * STAGE + (tid + 256 * i) * 16) = src[i];
+    for (int i = 0; i < APT; ++i) *(u32x4*)(sA + buf * STAGE + (tid + NTHR * i) * 16) = src[i];
     if (tid < BM) sSA[buf][tid] = sa;
   };
 
@@ -212,11 +215,13 @@ bool mfma_fp8_block(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of
                     hipStream_t st) {
   if (wp != WP_FP8_BLOCK || af != A_FP8 || stype != S_F32 || zero || t.bm != 128) return false;
   const dim3 grid(t.grid_x, t.grid_y, t.ksplit > 1 ? t.ksplit : 1);
+  constexpr int NW = 8;
 #define QG_FP8B(OF_)                                                                                        \
   if (of == OF_) {                                                                                          \
-    if (moe) hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, true, false>), grid, dim3(256), 0, st, a);      \
-    else if (t.ksplit > 1) hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, false, true>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, false, false>), grid, dim3(256), 0, st, a);         \
+    if (moe) hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, true, false, NW>), grid, dim3(64 * NW), 0, st, a); \
+    else if (t.ksplit > 1)                                                                                  \
+      hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, false, true, NW>), grid, dim3(64 * NW), 0, st, a);    \
+    else hipLaunchKernelGGL((mfma_fp8_block_kernel<OF_, false, false, NW>), grid, dim3(64 * NW), 0, st, a); \
     return true;                                                                                            \
   }
   QG_FP8B(O_BF16)
