@@ -80,6 +80,8 @@ def decode_act(x, a_type: str) -> np.ndarray:
         return decode_bf16(x)
     if a_type == "e4m3":
         return decode_e4m3(x)
+    if a_type == "e2m1":                       # packed codes [.., K/2], even k in the low nibble
+        return decode_e2m1(unpack_u8_nibbles(x))
     raise ValueError(a_type)
 
 

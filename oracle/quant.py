@@ -8,12 +8,21 @@ row), code = round-to-nearest-even onto the e4m3 value set of clamp(x / scale, +
 
 Rounding here is done by searching the 254 finite e4m3 values (nearest value; on a
 tie, the code with an even mantissa), independent of any library cast.
+
+MXFP4 activations (W4A4: "Humming" README, "Key Features", lists FP4 activations; the
+wiki article, "Quantization representation", names UE8M0 scales) are quantized per
+block of 32 consecutive K of a row.  The pages give no rule; the reading used is the
+OCP Microscaling (MX) v1.0 conversion: shared exponent E = floor(log2(max |block|)) - 2
+(2 = the largest e2m1 exponent), clamped to [-127, 127], stored as the UE8M0 byte E + 127
+(byte 0 for an all-zero block); each element becomes the e2m1 value nearest to
+x / 2^E (ties to the even code, values above 6 saturate to 6); a code is negative only
+when its magnitude is not zero.  Inputs must be finite.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_e4m3
+from .formats import decode_e2m1, decode_e4m3
 
 
 def _table():
@@ -55,3 +64,34 @@ def absmax_rows(x):
     scale[amax == 0] = np.float32(1.0)
     q = np.clip((x32 / scale[:, None]).astype(np.float32), -448.0, 448.0)
     return round_to_e4m3(q.astype(np.float64)), scale
+
+
+# the 8 non-negative e2m1 values, codes 0..7 in ascending order
+_E2M1 = decode_e2m1(np.arange(8))
+
+
+def round_to_e2m1(q) -> np.ndarray:
+    """Nearest e2m1 code (ties to the even code, saturating at 6) for each float64 q."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.minimum(np.abs(q), 6.0)
+    idx = np.clip(np.searchsorted(_E2M1, a), 1, 7)      # first value >= a
+    lo, hi = _E2M1[idx - 1], _E2M1[idx]
+    d_lo, d_hi = a - lo, hi - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (idx % 2 == 0))
+    mag = np.where(a == 0, 0, np.where(pick_hi, idx, idx - 1)).astype(np.int64)
+    return np.where((q < 0) & (mag != 0), mag | 8, mag).astype(np.uint8)
+
+
+def mxfp4_rows(x):
+    """x [M, K] (K % 32 == 0, finite) -> (packed e2m1 codes uint8 [M, K/2], UE8M0 bytes uint8 [M, K/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    m, k = x.shape
+    blocks = x.reshape(m, k // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))           # amax = f * 2^e, f in [0.5, 1)
+    shared = np.clip(e - 1 - 2, -127, 127)
+    shared = np.where(amax > 0, shared, -127)
+    q = blocks / np.exp2(shared)[:, :, None]
+    codes = round_to_e2m1(q).reshape(m, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (shared + 127).astype(np.uint8)

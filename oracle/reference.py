@@ -22,7 +22,8 @@ Readings where the pages are silent (each listed in the design notes):
 * zero points are integers in the code domain: w = (u - z) * s;
 * symmetric int4 keeps -8;
 * activations are what the kernel reads: f16/bf16 values, or sx[m] * e4m3(code) (with block
-  scales sx[m, k / 128] * e4m3(code));
+  scales sx[m, k / 128] * e4m3(code)), or MXFP4 activations 2^(b[m, k / 32] - 127) * e2m1(code)
+  (one UE8M0 exponent per 32 consecutive K of a row, as for MXFP4 weights);
 * block scales ("Humming" wiki article, "Quantization representation": a scale shared across
   both matrix dimensions): e4m3 weights with group G > 0 carry one scale per G x G block of
   (output channel, K);
@@ -94,6 +95,9 @@ def dequant_rows(layer, expert: int, rows) -> np.ndarray:
 def activations(acts, a_type: str) -> np.ndarray:
     """The activation values the kernel multiplies, in float64 [M, K]."""
     x = F.decode_act(acts.x, a_type)
+    if a_type == "e2m1":
+        sx = F.decode_ue8m0(acts.x_scale)        # [M, K / 32]
+        return x * np.repeat(sx, 32, axis=1)
     if a_type == "e4m3":
         sx = np.asarray(acts.x_scale, dtype=np.float32).astype(np.float64)
         if sx.ndim == 2:                       # one scale per (row, group of K / G columns)

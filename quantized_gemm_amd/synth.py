@@ -127,7 +127,7 @@ class Layer:
     """One quantized layer in storage form plus its activations."""
     name: str
     w_type: str            # "int4" | "uint4" | "e2m1" | "e4m3"
-    a_type: str            # "f16" | "bf16" | "e4m3"
+    a_type: str            # "f16" | "bf16" | "e4m3" | "e2m1"
     s_type: str            # "f16" | "bf16" | "f32" | "ue8m0"
     out_type: str          # "f16" | "bf16"
     n: int
@@ -143,8 +143,8 @@ class Layer:
 
 @dataclass
 class Acts:
-    x: np.ndarray                  # uint16 bits [M, K] (f16/bf16) or uint8 e4m3 codes [M, K]
-    x_scale: np.ndarray | None     # float32 [M] for e4m3 activations
+    x: np.ndarray                  # uint16 bits [M, K] (f16/bf16), uint8 e4m3 codes [M, K] or packed e2m1 [M, K/2]
+    x_scale: np.ndarray | None     # float32 [M] (or [M, K/128]) for e4m3, uint8 UE8M0 [M, K/32] for e2m1
     topk_ids: np.ndarray | None    # int32 [T, topk] for MoE
     topk_weights: np.ndarray | None = None   # float32 [T, topk]: router probabilities of the chosen experts
 
@@ -283,6 +283,37 @@ def moe_w4a8_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096
     return layer, Acts(xq, sx, ids, router_weights(logits, ids))
 
 
+def mxfp4_act_codes(rng, rows: int, k: int):
+    """Random MXFP4 activations as stored: packed e2m1 codes (every byte value equally likely) and
+    UE8M0 exponents 124..130 per 32 elements of a row."""
+    x = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    xs = (127 + rng.integers(-3, 4, size=(rows, k // 32), dtype=np.int64)).astype(np.uint8)
+    return x, xs
+
+
+def dense_w4a4_mxfp4(m: int = 16, n: int = 4096, k: int = 7168, out: str = "bf16", seed: int = 0):
+    """Dense W4A4 MXFP4: e2m1 weights with UE8M0 exponents 119..123 per 32 along K (as the W4A8
+    MXFP4 workload) times MXFP4 activations (random codes, exponents 124..130 per 32)."""
+    rng = _rng(seed)
+    w = rng.integers(0, 256, size=(1, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(1, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    x, xs = mxfp4_act_codes(rng, m, k)
+    layer = Layer("dense_w4a4_mxfp4", "e2m1", "e2m1", "ue8m0", out, n, k, 32, 1, w, s, None)
+    return layer, Acts(x, xs, None)
+
+
+def moe_w4a4_mxfp4(t: int = 16, experts: int = 128, topk: int = 8, n: int = 4096, k: int = 7168, seed: int = 0):
+    """MoE W4A4 MXFP4: the MXFP4 MoE workload's weights and routing with MXFP4 activations."""
+    rng = _rng(seed)
+    w = rng.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
+    s = (127 + rng.integers(-8, -3, size=(experts, n, k // 32), dtype=np.int64)).astype(np.uint8)
+    x, xs = mxfp4_act_codes(rng, t, k)
+    logits = rng.standard_normal((t, experts), dtype=np.float32)
+    ids = topk_from_logits(logits, topk)
+    layer = Layer("moe_w4a4_mxfp4", "e2m1", "e2m1", "ue8m0", "bf16", n, k, 32, experts, w, s, None)
+    return layer, Acts(x, xs, ids, router_weights(logits, ids))
+
+
 def moe_w4a8_int4(t: int = 64, experts: int = 64, topk: int = 6, n: int = 2816, k: int = 4096,
                   group: int = 128, hot_frac: float = 0.2, hot_experts=(0, 1, 2, 3), hot_bias: float = 3.0,
                   seed: int = 0):
@@ -387,4 +418,6 @@ WORKLOADS = {
     "dense_w4a8_mxfp4": dense_w4a8_mxfp4,
     "moe_w4a8_mxfp4": moe_w4a8_mxfp4,
     "dense_w8a8_fp8_block": dense_w8a8_fp8_block,
+    "dense_w4a4_mxfp4": dense_w4a4_mxfp4,
+    "moe_w4a4_mxfp4": moe_w4a4_mxfp4,
 }
