@@ -32,7 +32,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_gemm_amd", "csrc")
 # sources that define the MFMA-bound kernel (the dominant launch of the default sweep)
 MFMA_SOURCES = ["qg_mfma_kernel.h", "qg_device.h", "qg_kernels.h", "qg_mfma_int4.hip"]
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 
 # Workloads: (builder, sweep, arithmetic type of the MFMAs (selects the peak), description).
 # The W4A8 layer runs with the workspace qg_workspace_bytes asks for, so its products are
@@ -56,6 +56,12 @@ WORKLOADS = {
                                   "fp8 x fp4 MFMAs), N=K=8192; M sweep"),
     "moe_w4a8_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="fp8", moe=dict(experts=128, topk=8),
                            desc="MoE W4A8 MXFP4 (e2m1 + UE8M0/32 x per-token e4m3, scaled fp8 x fp4 MFMAs), E=128 "
+                                "top-8, fused gate+up N=4096, K=7168; T sweep"),
+    "dense_w4a4_mxfp4": dict(sweep=[1, 16, 128, 1024, 4096], n=8192, k=8192, dtype="fp4",
+                             desc="dense W4A4 MXFP4 (e2m1 + UE8M0/32 weights x e2m1 + UE8M0/32 activations, scaled "
+                                  "fp4 x fp4 MFMAs), N=K=8192; M sweep"),
+    "moe_w4a4_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="fp4", moe=dict(experts=128, topk=8),
+                           desc="MoE W4A4 MXFP4 (e2m1 + UE8M0/32 on both sides, scaled fp4 x fp4 MFMAs), E=128 "
                                 "top-8, fused gate+up N=4096, K=7168; T sweep"),
     "moe_w4a8_int4": dict(sweep=[64, 1024, 8192], n=2816, k=4096, dtype="bf16", moe=dict(experts=64, topk=6),
                           desc="MoE W4A8 int4 weights with bf16 group-128 scales x per-token e4m3 activations, "

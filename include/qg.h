@@ -62,8 +62,10 @@ enum { QG_W_INT4 = 1,      /* symmetric int4 in [-8, 7], two's-complement nibble
        QG_W_FP8_E4M3 = 4   /* OCP FP8 e4m3 ("fn") codes                                       */ };
 /* Scale types. */
 enum { QG_S_F16 = 1, QG_S_BF16 = 2, QG_S_F32 = 3, QG_S_UE8M0 = 4 };
-/* Activation types.  FP8 activations come with one float32 scale per row (token). */
-enum { QG_A_F16 = 1, QG_A_BF16 = 2, QG_A_FP8_E4M3 = 3 };
+/* Activation types.  FP8 activations come with one float32 scale per row (token); FP4
+ * activations (MXFP4: packed e2m1 codes, even K in the low nibble) with one UE8M0 exponent
+ * byte per 32 consecutive K of a row. */
+enum { QG_A_F16 = 1, QG_A_BF16 = 2, QG_A_FP8_E4M3 = 3, QG_A_FP4_E2M1 = 4 };
 /* Output types. */
 enum { QG_O_F16 = 1, QG_O_BF16 = 2 };
 /* Compute options. */
@@ -86,6 +88,8 @@ enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                 
  *       per channel), e4m3 activations                                 [W4A8]
  *   e2m1 weights, UE8M0 scales, group_k == 32, f16|bf16 activations  [MXFP4 W4A16]
  *   e2m1 weights, UE8M0 scales, group_k == 32, e4m3 activations      [MXFP4 W4A8]
+ *   e2m1 weights, UE8M0 scales, group_k == 32, e2m1 activations with UE8M0 exponents per
+ *       32 K ("Humming" README, "Key Features": FP4 activations)    [MXFP4 W4A4]
  *   e4m3 weights, f32 channel scales (group_k == 0), e4m3 activations [W8A8]
  *   e4m3 weights, f32 block scales (group_k == 128: one scale per 128 output channels x
  *       128 K, scales [E][N/128][K/128], n % 128 == 0), e4m3 activations with one f32
@@ -164,14 +168,16 @@ size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t top
 
 /*
  * qg_gemm: dense Y[m, n] = sum_k X[m, k] * W[n, k] for a prepared dense layer.
- *   x        device [M][K] of a_type (f16/bf16 values or e4m3 codes)
- *   x_scale  device float32 per-token scales for e4m3 activations, else NULL: [M], or
- *            [M][K/128] for block-scaled layers
+ *   x        device [M][K] of a_type (f16/bf16 values or e4m3 codes), or packed e2m1 codes
+ *            uint8 [M][K/2] for FP4 activations
+ *   x_scale  device, else NULL: float32 per-token scales for e4m3 activations, [M], or
+ *            [M][K/128] for block-scaled layers; uint8 UE8M0 exponents [M][K/32] for FP4
+ *            activations (X[m, k] = e2m1(code) * 2^(x_scale[m][k/32] - 127))
  *   y        device [M][N] of out_type, written in full (fp32 accumulation, RNE)
  *   ws       device workspace of ws_bytes >= qg_workspace_bytes(p, m, 0)
  * The tile / split-K choice is made from M on the host (the M-bucket selector).
  */
-qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, void* y, int64_t m,
+qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void* y, int64_t m,
                   void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -234,16 +240,16 @@ qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, i
 /*
  * qg_moe_gemm: grouped GEMM over the aligned rows.  For every (token t, slot j)
  * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
- *   x        device [T][K] of a_type;  x_scale device float32 [T] for e4m3 ([T][K/128] for
- *            block-scaled layers), else NULL
+ *   x        device [T][K] of a_type (FP4: uint8 [T][K/2]);  x_scale device float32 [T] for
+ *            e4m3 ([T][K/128] for block-scaled layers), uint8 [T][K/32] for FP4, else NULL
  *   sorted_ids / expert_ids / num_post_pad  from qg_moe_align with the same block_m
  *   block_m  4, 16, 32 or 64 (weight-streaming kernel) or 128, 256 (MFMA kernel; 256 not
- *            for e4m3 or int4->e4m3 weights); qg_moe_block_m picks one, any other is
- *            QG_ERR_UNSUPPORTED
+ *            for e4m3 or int4->e4m3 weights); FP4 activations: 16, 32, 64 or 128;
+ *            qg_moe_block_m picks one, any other is QG_ERR_UNSUPPORTED
  *   y        device [T*topk][N] of out_type; rows of dropped slots are not written
  * The grid is sized from capacity; blocks past num_post_pad exit at once.
  */
-qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
+qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, const int32_t* sorted_ids,
                       const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
                       int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream);
 
@@ -290,6 +296,22 @@ qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_
  */
 qg_status qg_quantize_e4m3_rows(const void* x, int64_t rows, int64_t k, int32_t in_type, uint8_t* codes, float* scale,
                                 void* stream);
+
+/*
+ * qg_quantize_e2m1_rows: MXFP4 quantization of 16-bit activations, the input of the W4A4
+ * products ("Humming" README, "Key Features": FP4 activations and UE8M0 scales).  The pages
+ * give no rule; this is the OCP Microscaling v1.0 conversion.  For each block of 32
+ * consecutive elements of a row of x (device [rows][k], in_type QG_A_F16 / QG_A_BF16, finite):
+ *   E = floor(log2(max |block|)) - 2, clamped to [-127, 127] (-127 for an all-zero block),
+ *   scales[r][b] = E + 127 (UE8M0);
+ *   each element's code = the e2m1 value nearest to x / 2^E, ties to the even code, values
+ *   above 6 in magnitude give 6; negative codes only for non-zero magnitudes.
+ *   codes  device uint8 [rows][k/2], 16-byte aligned (even k in the low nibble)
+ *   scales device uint8 [rows][k/32]
+ * k % 32 == 0, else QG_ERR_UNSUPPORTED.
+ */
+qg_status qg_quantize_e2m1_rows(const void* x, int64_t rows, int64_t k, int32_t in_type, uint8_t* codes,
+                                uint8_t* scales, void* stream);
 
 /*
  * qg_moe_combine: out[t][:] = sum over slots j with 0 <= topk_ids[t][j] < E of

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqg.so")
 # Enumerations (values as in include/qg.h).
 W_INT4, W_UINT4, W_FP4_E2M1, W_FP8_E4M3 = 1, 2, 3, 4
 S_F16, S_BF16, S_F32, S_UE8M0 = 1, 2, 3, 4
-A_F16, A_BF16, A_FP8_E4M3 = 1, 2, 3
+A_F16, A_BF16, A_FP8_E4M3, A_FP4_E2M1 = 1, 2, 3, 4
 O_F16, O_BF16 = 1, 2
 C_NATIVE, C_W_TO_FP8, C_BATCH_INVARIANT = 0, 1, 4
 MOE_CONTIGUOUS, MOE_MASKED = 1, 2
@@ -29,7 +29,7 @@ STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_E
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
            "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine",
-           "qg_quantize_e4m3_rows", "qg_dequant", "qg_status_str", "qg_version"]
+           "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_status_str", "qg_version"]
 
 
 class QGError(RuntimeError):
@@ -82,6 +82,7 @@ def lib():
         L.qg_moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, i32, vp, vp]
         L.qg_moe_combine.restype = i32
         L.qg_quantize_e4m3_rows.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.qg_quantize_e2m1_rows.argtypes, L.qg_quantize_e2m1_rows.restype = [vp, i64, i64, i32, vp, vp, vp], i32
         L.qg_quantize_e4m3_rows.restype = i32
         L.qg_dequant.argtypes, L.qg_dequant.restype = [pp, i32, vp, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
@@ -202,6 +203,12 @@ def quantize_e4m3_rows(x, rows: int, k: int, in_type: int, codes, scale, stream=
     """Per-token absmax e4m3 quantization of 16-bit rows: codes [rows][k] uint8, scale [rows] float32."""
     st = lib().qg_quantize_e4m3_rows(_ptr(x), rows, k, in_type, _ptr(codes), _ptr(scale), _stream(stream))
     _check(st, "qg_quantize_e4m3_rows")
+
+
+def quantize_e2m1_rows(x, rows: int, k: int, in_type: int, codes, scales, stream=None):
+    """MXFP4 quantization of 16-bit rows: codes [rows][k/2] uint8 (packed e2m1), scales [rows][k/32] uint8."""
+    st = lib().qg_quantize_e2m1_rows(_ptr(x), rows, k, in_type, _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "qg_quantize_e2m1_rows")
 
 
 def dequant(p: Prepared, expert: int, out, stream=None):

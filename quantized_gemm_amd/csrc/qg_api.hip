@@ -85,7 +85,7 @@ qg_status check_desc(const qg_layer_desc* dd, PathInfo* pi) {
   const qg_layer_desc* d = &dv;
   if (d->w_type < QG_W_INT4 || d->w_type > QG_W_FP8_E4M3) return QG_ERR_INVALID_ARG;
   if (d->s_type < QG_S_F16 || d->s_type > QG_S_UE8M0) return QG_ERR_INVALID_ARG;
-  if (d->a_type < QG_A_F16 || d->a_type > QG_A_FP8_E4M3) return QG_ERR_INVALID_ARG;
+  if (d->a_type < QG_A_F16 || d->a_type > QG_A_FP4_E2M1) return QG_ERR_INVALID_ARG;
   if (d->out_type != QG_O_F16 && d->out_type != QG_O_BF16) return QG_ERR_INVALID_ARG;
   if (d->compute != QG_C_NATIVE && d->compute != QG_C_W_TO_FP8) return QG_ERR_INVALID_ARG;
   if (d->has_zero != 0 && d->has_zero != 1) return QG_ERR_INVALID_ARG;
@@ -123,6 +123,8 @@ qg_status check_desc(const qg_layer_desc* dd, PathInfo* pi) {
     if (act16) {
       if (d->out_type != (d->a_type == QG_A_F16 ? QG_O_F16 : QG_O_BF16)) return QG_ERR_UNSUPPORTED;
       p.af = d->a_type == QG_A_F16 ? A_F16 : A_BF16;
+    } else if (d->a_type == QG_A_FP4_E2M1) {
+      p.af = A_FP4;   // W4A4 MXFP4: both operands and both exponents go to the scaled fp4 MFMA
     } else {
       p.af = A_FP8;   // W4A8 MXFP4: e2m1 codes and UE8M0 scales are operands of the scaled fp8/fp4 MFMA
     }
@@ -302,6 +304,7 @@ MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
 
 // Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
+  if (pi.af == A_FP4) return 0;   // W4A4 splits K only inside a workgroup
   if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
@@ -396,16 +399,28 @@ static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
   a.z_bytes = (uint32_t)(p->z_expert_bytes * p->desc.num_experts);
 }
 
+// W4A4 rows per workgroup for a dense product: 16 / 32 / 64-row workgroups (K split over 8
+// waves) while the 128 x 128 tiles would leave the GPU under-filled, 128 x 128 tiles above;
+// batch-invariant: 128 x 128 tiles for every M (each output then one wave's full K loop).
+int w4a4_dense_rows(int64_t m, int64_t n, bool binv) {
+  if (binv) return 128;
+  if (m <= 16) return 16;
+  if (m <= 32) return 32;
+  const int64_t big = ((m + 127) / 128) * ((n + 127) / 128);
+  return big >= 512 ? 128 : 64;
+}
+
 // Buffer-resource limits of the kernels: every region a kernel addresses must stay
 // below 2^31 bytes (one expert's weights, all scales, the activations).
 bool fits_rsrc(const qg_prepared* p, int64_t x_rows) {
   const int64_t lim = (int64_t)1 << 31;
-  const int64_t ab = p->desc.a_type == QG_A_FP8_E4M3 ? 1 : 2;
+  const int64_t row_bytes = p->desc.a_type == QG_A_FP8_E4M3 ? p->desc.k
+                            : p->desc.a_type == QG_A_FP4_E2M1 ? p->desc.k / 2 : p->desc.k * 2;
   return (int64_t)p->w_expert_bytes < lim && (int64_t)(p->s_expert_bytes * p->desc.num_experts) < lim &&
-         (int64_t)(p->z_expert_bytes * p->desc.num_experts) < lim && x_rows * p->desc.k * ab < lim;
+         (int64_t)(p->z_expert_bytes * p->desc.num_experts) < lim && x_rows * row_bytes < lim;
 }
 
-qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, void* y, int64_t m, void* ws,
+qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void* y, int64_t m, void* ws,
                   size_t ws_bytes, void* stream) {
   PathInfo pi;
   qg_status s = check_prepared(p, &pi);
@@ -414,14 +429,20 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const float* x_scale, voi
   if (m < 0) return QG_ERR_INVALID_ARG;
   if (m == 0) return QG_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return QG_ERR_INVALID_ARG;
-  if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
+  if ((p->desc.a_type == QG_A_FP8_E4M3 || p->desc.a_type == QG_A_FP4_E2M1) && !x_scale) return QG_ERR_INVALID_ARG;
   if (m > (1 << 24) || !fits_rsrc(p, m)) return QG_ERR_UNSUPPORTED;
   s = check_arch();
   if (s != QG_OK) return s;
   StreamArgs a{};
   fill_stream_args(a, p);
-  a.x = x; a.x_scale = x_scale; a.y = y; a.m = m; a.x_rows = m;
+  a.x = x; a.x_scale = (const float*)x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
+  if (pi.af == A_FP4) {
+    const int bm = w4a4_dense_rows(m, p->desc.n, pi.binv != 0);
+    QG_LOG("gemm m=%lld n=%lld k=%lld -> w4a4 rows=%d", (long long)m, (long long)p->desc.n, (long long)p->desc.k, bm);
+    if (!launch_w4a4(a, bm, false, pi.of, 1, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
   if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     if (t.ksplit > 1) {
@@ -500,6 +521,11 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   // which costs more than the occasional second pass over an expert's weights).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
+  if (pi.af == A_FP4) {   // W4A4 blocks: 16, 32, 64 or 128 rows, the busier experts' counts fitting
+    if (pi.binv) return 128;
+    const double busy = mean + 3.0 * sqrt(mean);
+    return busy <= 16 ? 16 : busy <= 32 ? 32 : busy <= 64 ? 64 : 128;
+  }
   if (pi.binv) return (mean < 512 || !mfma_rows256(pi)) ? 128 : 256;   // MFMA blocks at every size
   if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
@@ -562,7 +588,7 @@ qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, i
   return launched();
 }
 
-qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale, const int32_t* sorted_ids,
+qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, const int32_t* sorted_ids,
                       const int32_t* expert_ids, const int32_t* num_post_pad, int64_t tokens, int32_t topk,
                       int32_t block_m, void* y, void* ws, size_t ws_bytes, void* stream) {
   PathInfo pi;
@@ -572,9 +598,10 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   if (tokens == 0) return QG_OK;
   if (!x || !y || !sorted_ids || !expert_ids || !num_post_pad || !aligned16(x) || !aligned16(y))
     return QG_ERR_INVALID_ARG;
-  if (p->desc.a_type == QG_A_FP8_E4M3 && !x_scale) return QG_ERR_INVALID_ARG;
+  if ((p->desc.a_type == QG_A_FP8_E4M3 || p->desc.a_type == QG_A_FP4_E2M1) && !x_scale) return QG_ERR_INVALID_ARG;
   if (block_m != 4 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256)
     return QG_ERR_UNSUPPORTED;
+  if (pi.af == A_FP4 && (block_m == 4 || block_m == 256)) return QG_ERR_UNSUPPORTED;
   if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (pi.binv && block_m <= kStreamMaxRows) return QG_ERR_UNSUPPORTED;   // one MMA type for every size
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
@@ -584,9 +611,14 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const float* x_scale,
   qg_moe_capacity(tokens, topk, p->desc.num_experts, block_m, &cs, &cb);
   StreamArgs a{};
   fill_stream_args(a, p);
-  a.x = x; a.x_scale = x_scale; a.y = y; a.m = 0; a.x_rows = tokens;
+  a.x = x; a.x_scale = (const float*)x_scale; a.y = y; a.m = 0; a.x_rows = tokens;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.num_post_pad = num_post_pad;
   a.topk = topk; a.sentinel = (int)(tokens * topk);
+  if (pi.af == A_FP4) {
+    QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> w4a4 grid_y=%lld", (long long)tokens, topk, block_m, (long long)cb);
+    if (!launch_w4a4(a, block_m, true, pi.of, (unsigned)cb, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
+    return launched();
+  }
   if (block_m > kStreamMaxRows) {
     MfmaTile t{};
     t.bm = block_m;
@@ -658,6 +690,21 @@ qg_status qg_quantize_e4m3_rows(const void* x, int64_t rows, int64_t k, int32_t 
   return launched();
 }
 
+qg_status qg_quantize_e2m1_rows(const void* x, int64_t rows, int64_t k, int32_t in_type, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+  if (rows < 0 || k <= 0) return QG_ERR_INVALID_ARG;
+  if (in_type != QG_A_F16 && in_type != QG_A_BF16) return QG_ERR_INVALID_ARG;
+  if (k % 32 != 0) return QG_ERR_UNSUPPORTED;
+  if (rows > ((int64_t)1 << 31) - 1 || rows * (k / 32) > ((int64_t)1 << 36)) return QG_ERR_UNSUPPORTED;
+  if (rows == 0) return QG_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return QG_ERR_INVALID_ARG;
+  qg_status s = check_arch();
+  if (s != QG_OK) return s;
+  if (!launch_quant_rows_e2m1(x, rows, k, in_type == QG_A_F16 ? A_F16 : A_BF16, codes, scales, (hipStream_t)stream))
+    return QG_ERR_UNSUPPORTED;
+  return launched();
+}
+
 qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* topk_ids, int64_t tokens, int32_t topk,
                          int32_t num_experts, int64_t n, int32_t dtype, void* out, void* stream) {
   if (tokens < 0 || topk <= 0 || num_experts <= 0 || n <= 0) return QG_ERR_INVALID_ARG;
@@ -693,7 +740,8 @@ qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* str
   a.n = (int)p->desc.n; a.k = (int)p->desc.k;
   a.groups = p->desc.group_k == 0 ? 1 : (int)(p->desc.k / p->desc.group_k);
   a.group = p->desc.group_k;
-  a.wp = pi.dq_wp; a.af = pi.dq_wp == WP_FP4 && pi.af == A_FP8 ? A_BF16 : pi.af;   // e2m1 reads back through bf16
+  a.wp = pi.dq_wp;   // e2m1 under fp8 / fp4 activations reads back through bf16
+  a.af = pi.dq_wp == WP_FP4 && (pi.af == A_FP8 || pi.af == A_FP4) ? A_BF16 : pi.af;
   a.stype = pi.st; a.zero = p->desc.has_zero;
   launch_dequant(a, (hipStream_t)stream);
   return launched();

@@ -29,7 +29,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Formats (template tags) ---------------------------------------------------------
-enum : int { A_F16 = 1, A_BF16 = 2, A_FP8 = 3 };
+enum : int { A_F16 = 1, A_BF16 = 2, A_FP8 = 3, A_FP4 = 4 };
 enum : int { O_F16 = 1, O_BF16 = 2 };
 enum : int { S_F16 = 1, S_BF16 = 2, S_F32 = 3, S_UE8M0 = 4 };
 // Weight paths of the kernels.
@@ -185,6 +185,11 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
 // activation operand's scale is neutral.  The e2m1 operand uses the low 4 dwords of b.
 __device__ __forceinline__ f32x4 mfma16x16x128_fp8_fp4(i32x8 a, i32x8 b, int sb, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
+}
+
+// e2m1 x e2m1 with E8M0 block exponents for both operands (format code 4 for A and B)
+__device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp4(i32x8 a, i32x8 b, int sa, int sb, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
 
 template <int AF>

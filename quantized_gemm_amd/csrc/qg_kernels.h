@@ -79,6 +79,13 @@ bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int ou
 // Per-row absmax e4m3 quantization of 16-bit rows (in_t O_F16 / O_BF16), k <= 8192, k % 8 == 0.
 bool launch_quant_rows_e4m3(const void* x, int64_t rows, int64_t k, int in_t, void* codes, float* scale,
                             hipStream_t st);
+// W4A4 MXFP4 (qg_w4a4.hip): e2m1 x e2m1 with UE8M0 exponents on both sides.  bm = rows per
+// workgroup (16, 32, 64 or 128; MoE: the align block); dense: grid over a.m, MoE: grid_y blocks.
+int w4a4_cols(int bm);
+bool launch_w4a4(const StreamArgs& a, int bm, bool moe, int of, unsigned grid_y, hipStream_t st);
+// MXFP4 quantization of 16-bit rows (in_t A_F16 / A_BF16), k % 32 == 0.
+bool launch_quant_rows_e2m1(const void* x, int64_t rows, int64_t k, int in_t, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st);
 bool launch_combine(const void* y, const float* w, const int32_t* ids, int64_t tokens, int topk, int experts, int64_t n,
                     int dtype, void* out, hipStream_t st);
 

@@ -8,12 +8,12 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (A_BF16, A_F16, A_FP8_E4M3, C_NATIVE, C_W_TO_FP8, O_BF16, O_F16, S_BF16, S_F16, S_F32, S_UE8M0,
+from . import (A_BF16, A_F16, A_FP4_E2M1, A_FP8_E4M3, C_NATIVE, C_W_TO_FP8, O_BF16, O_F16, S_BF16, S_F16, S_F32, S_UE8M0,
                W_FP4_E2M1, W_FP8_E4M3, W_INT4, W_UINT4, make_desc, prepare, prepared_bytes)
 
 _W = {"int4": W_INT4, "uint4": W_UINT4, "e2m1": W_FP4_E2M1, "e4m3": W_FP8_E4M3}
 _S = {"f16": S_F16, "bf16": S_BF16, "f32": S_F32, "ue8m0": S_UE8M0}
-_A = {"f16": A_F16, "bf16": A_BF16, "e4m3": A_FP8_E4M3}
+_A = {"f16": A_F16, "bf16": A_BF16, "e4m3": A_FP8_E4M3, "e2m1": A_FP4_E2M1}
 _O = {"f16": O_F16, "bf16": O_BF16}
 _TORCH_OUT = {"f16": torch.float16, "bf16": torch.bfloat16}
 

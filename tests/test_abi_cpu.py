@@ -197,3 +197,30 @@ def test_quantize_rows_rejects_on_the_host():
     assert lib.qg_quantize_e4m3_rows(fake, 4, 8200, qg.A_BF16, fake, fake, None) == 2
     assert lib.qg_quantize_e4m3_rows(fake, 4, 64, qg.A_BF16, None, fake, None) == 1
     assert lib.qg_quantize_e4m3_rows(ctypes.c_void_p(4100), 4, 64, qg.A_BF16, fake, fake, None) == 1
+
+
+def test_w4a4_descriptions():
+    # MXFP4 activations pair only with MXFP4 weights (e2m1, UE8M0 per 32, no zeros, native)
+    mx = dict(w_type=qg.W_FP4_E2M1, s_type=qg.S_UE8M0, group_k=32, has_zero=0, a_type=qg.A_FP4_E2M1)
+    layer = synth.dense_w4a4_mxfp4(m=1, n=64, k=256)[0]
+    sz = L.sizes(layer.w_type, layer.s_type, layer.n, layer.k, layer.group, layer.experts, False)
+    assert qg.prepared_bytes(layers.desc_for(layer)) == sz["total"]
+    assert qg.prepared_bytes(_desc(**mx)) > 0
+    assert qg.prepared_bytes(_desc(**dict(mx, out_type=qg.O_F16))) > 0
+    assert qg.prepared_bytes(_desc(**dict(mx, group_k=64))) == 0
+    assert qg.prepared_bytes(_desc(**dict(mx, compute=qg.C_W_TO_FP8))) == 0
+    assert qg.prepared_bytes(_desc(a_type=qg.A_FP4_E2M1)) == 0                      # uint4 weights
+    assert qg.prepared_bytes(_desc(w_type=qg.W_FP8_E4M3, s_type=qg.S_F32, group_k=0, has_zero=0,
+                                   a_type=qg.A_FP4_E2M1)) == 0
+    assert qg.prepared_bytes(_desc(**dict(mx, a_type=5))) == 0
+
+
+def test_quantize_e2m1_rows_rejects_on_the_host():
+    lib = qg.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.qg_quantize_e2m1_rows(fake, 0, 64, qg.A_BF16, fake, fake, None) == 0         # no rows: no-op
+    assert lib.qg_quantize_e2m1_rows(fake, 4, 64, qg.A_FP4_E2M1, fake, fake, None) == 1     # input must be 16-bit
+    assert lib.qg_quantize_e2m1_rows(fake, 4, 48, qg.A_BF16, fake, fake, None) == 2          # k % 32
+    assert lib.qg_quantize_e2m1_rows(fake, 4, 64, qg.A_BF16, None, fake, None) == 1
+    assert lib.qg_quantize_e2m1_rows(fake, 4, 64, qg.A_BF16, ctypes.c_void_p(4104), fake, None) == 1   # codes 16-B
+    assert lib.qg_quantize_e2m1_rows(ctypes.c_void_p(4100), 4, 64, qg.A_BF16, fake, fake, None) == 1
