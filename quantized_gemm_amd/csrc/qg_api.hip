@@ -438,6 +438,22 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
   a.x = x; a.x_scale = (const float*)x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
   if (pi.af == A_FP4) {
+    // enough 256-column tiles to fill the GPU and whole 256-wide K steps: the MFMA kernel
+    // (activations staged through LDS, 32x32x64 fp4 MFMAs), else the W4A4 kernel
+    if (!pi.binv && m > 64 && p->desc.k % 256 == 0) {
+      MfmaTile t{};
+      t.bm = 128;
+      t.grid_x = (unsigned)(((m + 127) / 128) * ((p->desc.n + 255) / 256));
+      t.grid_y = 1;
+      t.ksplit = 1;
+      if (t.grid_x >= (unsigned)kCUs) {
+        QG_LOG("gemm m=%lld n=%lld k=%lld -> fp4 mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
+               (long long)p->desc.k, t.bm, t.grid_x);
+        if (!launch_mfma_gemm(a, t, WP_FP4, A_FP4, pi.of, S_UE8M0, false, false, (hipStream_t)stream))
+          return QG_ERR_UNSUPPORTED;
+        return launched();
+      }
+    }
     const int bm = w4a4_dense_rows(m, p->desc.n, pi.binv != 0);
     QG_LOG("gemm m=%lld n=%lld k=%lld -> w4a4 rows=%d", (long long)m, (long long)p->desc.n, (long long)p->desc.k, bm);
     if (!launch_w4a4(a, bm, false, pi.of, 1, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
@@ -615,6 +631,17 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, 
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.num_post_pad = num_post_pad;
   a.topk = topk; a.sentinel = (int)(tokens * topk);
   if (pi.af == A_FP4) {
+    if (block_m == 128 && p->desc.k % 256 == 0) {
+      MfmaTile t{};
+      t.bm = 128;
+      t.grid_x = (unsigned)((p->desc.n + 255) / 256);
+      t.grid_y = (unsigned)cb;
+      t.ksplit = 1;
+      QG_LOG("moe_gemm T=%lld topk=%d bm=128 -> fp4 mfma grid=%ux%u", (long long)tokens, topk, t.grid_x, t.grid_y);
+      if (!launch_mfma_gemm(a, t, WP_FP4, A_FP4, pi.of, S_UE8M0, false, true, (hipStream_t)stream))
+        return QG_ERR_UNSUPPORTED;
+      return launched();
+    }
     QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> w4a4 grid_y=%lld", (long long)tokens, topk, block_m, (long long)cb);
     if (!launch_w4a4(a, block_m, true, pi.of, (unsigned)cb, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
     return launched();

@@ -192,6 +192,10 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp4(i32x8 a, i32x8 b, int sa,
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
 
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4_fp4(i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
 template <int AF>
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (AF == A_F16)
@@ -229,6 +233,10 @@ __device__ __forceinline__ void keep_in_vgprs(const f32x16& v) { asm volatile(""
 // there directly, the host pass drops the templates' launch stubs.
 __device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+// 4 bytes per lane into LDS: lane l writes lds + 4 l (lds wave-uniform); out of range: zeros.
+__device__ __forceinline__ void bload4_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
 }
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);

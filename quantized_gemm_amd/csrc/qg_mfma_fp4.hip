@@ -14,6 +14,11 @@ bool mfma_fp4(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int 
     return launch_mfma_variant<WP_FP4, A_FP8, O_BF16, S_UE8M0, false>(a, t, moe, st);
   if (wp == WP_FP4 && af == A_FP8 && of == O_F16 && stype == S_UE8M0 && zero == false)
     return launch_mfma_variant<WP_FP4, A_FP8, O_F16, S_UE8M0, false>(a, t, moe, st);
+  // e2m1 activations (W4A4 MXFP4): scaled fp4 x fp4 MFMAs
+  if (wp == WP_FP4 && af == A_FP4 && of == O_BF16 && stype == S_UE8M0 && zero == false)
+    return launch_mfma_variant<WP_FP4, A_FP4, O_BF16, S_UE8M0, false>(a, t, moe, st);
+  if (wp == WP_FP4 && af == A_FP4 && of == O_F16 && stype == S_UE8M0 && zero == false)
+    return launch_mfma_variant<WP_FP4, A_FP4, O_F16, S_UE8M0, false>(a, t, moe, st);
   return false;
 }
 

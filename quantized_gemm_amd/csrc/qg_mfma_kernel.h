@@ -33,10 +33,11 @@ namespace qg {
 template <int WP, int AF, int OF, int ST, bool ZERO, int BM, bool MOE, bool SPLIT, int CW>
 __global__ __launch_bounds__(64 * CW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mfma_gemm_kernel(MfmaArgs a) {
-  constexpr bool F8 = (AF == A_FP8);                 // e4m3 activations: fp8 MFMAs
-  constexpr bool FP4B = F8 && WP == WP_FP4;           // ... with e2m1 weights as the second operand
+  constexpr bool F4A = (AF == A_FP4);                // e2m1 activations: fp4 x fp4 MFMAs
+  constexpr bool F8 = (AF == A_FP8) || F4A;          // byte operands to scaled / fp8 MFMAs as stored
+  constexpr bool FP4B = (AF == A_FP8) && WP == WP_FP4;   // e4m3 activations with e2m1 weights
   constexpr int AB = F8 ? 1 : 2;
-  constexpr int BK = F8 ? 128 : 64;          // K per step; one LDS row segment = 128 bytes
+  constexpr int BK = F4A ? 256 : F8 ? 128 : 64;   // K per step; one LDS row segment = 128 bytes
   constexpr int NTHR = 64 * CW;              // CW waves, each owning BN / CW columns and all BM rows
   constexpr int MT = BM / 32;                // 32-row MFMA tiles per wave
   constexpr int WCOL = 256 / CW;             // columns per wave: 64 (4 waves) or 32 (8 waves)
@@ -46,7 +47,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int STAGE = BM * ROWB;
   constexpr int NS = 3;                      // activation stages in LDS (ring)
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
-  constexpr int BU = F8 ? (FP4B ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step
+  constexpr int BU = F8 ? (FP4B ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step (F4A: 4)
   // elements held by the bytes of the low / high nibble words of a 4-bit code word
   constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
   constexpr int M0[4] = {0, QUAD ? 1 : 4, QUAD ? 2 : 1, QUAD ? 3 : 5};
@@ -65,6 +66,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sS0[SREG];
   __shared__ __attribute__((aligned(16))) uint8_t sS1[SREG];
   __shared__ __attribute__((aligned(16))) uint8_t sS2[SREG];
+  // e2m1 activations: the step's UE8M0 exponents of each tile row (8 bytes: K groups
+  // 8 step .. 8 step + 7), one region per activation stage, loaded with that stage
+  constexpr int XSB = F4A ? BM * 8 : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[XSB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[XSB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX2[XSB];
   __shared__ int sRowTok[BM];
   __shared__ int sRowOut[BM];    // output row of each tile row (-1: none)
 
@@ -93,7 +100,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
     const int mtiles = (int)((a.m + BM - 1) / BM);
     const int ntiles = (int)gridDim.x / mtiles;
     const int id = blockIdx.x;
-    const int64_t rowb = (int64_t)a.k * AB, colb = WP == WP_FP8 ? a.k : a.k / 2;   // bytes per row / column
+    const int64_t rowb = F4A ? a.k / 2 : (int64_t)a.k * AB, colb = WP == WP_FP8 ? a.k : a.k / 2;   // bytes per row / column
     int xr = 0;
     int64_t best = 0;
     for (int cand = 1; cand <= 8; cand <<= 1) {
@@ -140,7 +147,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   const int ngroups = a.group == 0 ? 1 : a.k / a.group;
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)a.w_expert_bytes);
-  const int64_t xrow_bytes = (int64_t)a.k * AB;
+  const int64_t xrow_bytes = F4A ? a.k / 2 : (int64_t)a.k * AB;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(a.x_rows * xrow_bytes));
 
   // ---- activation staging: piece p of a step = (row p/8, physical chunk p%8) --------
@@ -165,6 +172,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
   auto issue_a = [&](int step, uint8_t* stage) {
 #pragma unroll
     for (int i = 0; i < APT; ++i) issue_a_piece(step, stage, i);
+  };
+  // e2m1 activations: dword h of tile row r's step exponents comes from thread 2r + h (a
+  // wave-uniform subset of the threads), into region + 4 tid; issued just before the same
+  // step's activations, so the wait for those covers it too.
+  int xs_off = -1;
+  if constexpr (F4A) {
+    if (tid < 2 * BM) {
+      const int tok = sRowTok[tid >> 1];
+      xs_off = tok < 0 ? -1 : tok * (a.k >> 5) + 4 * (tid & 1);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t xsr = make_rsrc(a.x_scale, F4A ? (uint32_t)(a.x_rows * (a.k >> 5)) : 0u);
+  auto issue_xs = [&](int step, uint8_t* reg) {
+    if constexpr (F4A) {
+      if (tid < 2 * BM)
+        bload4_lds(xsr, reg + (tid & ~63) * 4, xs_off < 0 || step >= nsteps ? kOOB : xs_off + 8 * (kstep0 + step));
+    }
   };
 
   // ---- scale and zero records: 16 bytes per lane, one load on wave 0 (scales) and one
@@ -242,9 +266,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
       for (int u = 0; u < BU; ++u) {
         // 4-bit: unit (step*2 + g) covers k = 64*step + 32g ..; fp8: units 8*step + 4g + u;
         // e2m1 under e4m3 activations: unit 4*step + 2u + g covers k = 128*step + 64u + 32g ..,
-        // the e2m1 operand of MFMA u on this lane
+        // the e2m1 operand of MFMA u on this lane; under e2m1 activations unit 8*step + 2u + g
+        // (k = 256*step + 64u + 32g ..), the operand of MFMA u
         const int64_t gs = (int64_t)(kstep0 + step);
-        const int64_t ku = F8 ? (FP4B ? gs * 4 + 2 * u + g : gs * 8 + 4 * g + u) : (gs * 2 + g);
+        const int64_t ku = F4A ? gs * 8 + 2 * u + g : F8 ? (FP4B ? gs * 4 + 2 * u + g : gs * 8 + 4 * g + u) : (gs * 2 + g);
         const bool ok = wok[t] && step < nsteps;
         // cached: every weight tile is read again by the other row tiles of the XCD
         dst[t][u] = bload16(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
@@ -256,7 +281,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t nb = min((int64_t)nb_count - 1, wcol[t] >> 4), c = wcol[t] & 15;
-      if constexpr (FP4B) {
+      if constexpr (F4A) {
+        // the UE8M0 exponents of the lane's four units (groups 8*step + 2u + g), bytes 0..3
+        // of one word kept in the float slot as raw bits; the MFMAs apply them
+        const uint8_t* sp = (const uint8_t*)a.s + (((int64_t)expert * nb_count + nb) * ngroups +
+                                                   (int64_t)(kstep0 + step) * 8 + g) * 16 + c;
+        s[t] = __uint_as_float((uint32_t)sp[0] | ((uint32_t)sp[32] << 8) | ((uint32_t)sp[64] << 16) |
+                               ((uint32_t)sp[96] << 24));
+        zs[t] = 0.f;
+      } else if constexpr (FP4B) {
         // the UE8M0 exponents of the lane's two units (groups 4*step + 2u + g), bytes 0 and 1
         // of one word kept in the float slot as raw bits; the MFMA applies them
         const uint8_t* sp = (const uint8_t*)a.s + (((int64_t)expert * nb_count + nb) * ngroups +
@@ -314,12 +347,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   issue_sz(1, sS0);
+  issue_xs(0, sX0);
   issue_a(0, sA0);
   __builtin_amdgcn_sched_barrier(0);
   load_b(DIST - 2, bw[DIST - 2]);
   if constexpr (F8) load_scale(min(DIST - 2, nsteps - 1), scl[DIST - 2], zsl[DIST - 2]);
   __builtin_amdgcn_sched_barrier(0);
   issue_sz(2, sS1);
+  issue_xs(1, sX1);
   issue_a(1, sA1);
   __builtin_amdgcn_sched_barrier(0);
   load_b(DIST - 1, bw[DIST - 1]);
@@ -411,6 +446,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
     uint8_t* const sAb = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
     uint8_t* const sAn = S == 0 ? sA2 : S == 1 ? sA0 : sA1;   // stage of step + 2
     const uint8_t* const sSb = S == 0 ? sS0 : S == 1 ? sS1 : sS2;
+    const uint8_t* const sXb = S == 0 ? sX0 : S == 1 ? sX1 : sX2;
+    uint8_t* const sXn = S == 0 ? sX2 : S == 1 ? sX0 : sX1;   // exponents of step + 2
     constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     uint8_t* const sSn = S == 0 ? sS2 : S == 1 ? sS0 : sS1;
     // this wave's A(step) loads have landed; the barrier makes every wave's visible and
@@ -429,6 +466,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_sz(step + 3, sSn);
+    issue_xs(step + 2, sXn);
     if constexpr (F8) issue_a(step + 2, sAn);   // 16-bit: one piece per sub-step, below
     __builtin_amdgcn_sched_barrier(0);
     constexpr int SL = (S + DIST) % 3;                        // slot of step + DIST
@@ -451,7 +489,41 @@ void mfma_gemm_kernel(MfmaArgs a) {
     };
     if constexpr (F8) pin_scales();
 
-    if constexpr (F8) {
+    if constexpr (F4A) {
+      // 4 x MT MFMAs per step (K quarters j, row tiles mt), 32x32x64 with both operands e2m1:
+      // lane (r, g) gives row r's K 64j + 32g .. + 31 (16 bytes, chunk 2j + g of the row
+      // segment) and its exponent; fragments are read two MFMAs ahead as in the e4m3 loop
+      auto read_a4 = [&](int q, int& sa) -> i32x8 {
+        const int j = q / MT, mt = q % MT;
+        const int row = 32 * mt + r;
+        const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * ((2 * j + g) ^ ((row >> 1) & 7)));
+        sa = sXb[row * 8 + 2 * j + g];
+        i32x8 A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = 0; }
+        return A;
+      };
+      constexpr int NQ = 4 * MT;
+      i32x8 Af4[3];
+      int sa4[3];
+      Af4[0] = read_a4(0, sa4[0]);
+      Af4[1] = read_a4(1, sa4[1]);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int j = q / MT, mt = q % MT;
+        if (q + 2 < NQ) Af4[(q + 2) % 3] = read_a4(q + 2, sa4[(q + 2) % 3]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          i32x8 B;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { B[i] = (int)b0[t][j][i]; B[4 + i] = 0; }
+          acc[mt][t] = mfma32x32x64_fp4_fp4(Af4[q % 3], B, sa4[q % 3],
+                                            (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu), acc[mt][t]);
+          keep_in_vgprs(acc[mt][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (F8) {
       // 2 x MT MFMA pairs per step (k halves j, row tiles mt); each pair's activation
       // fragment is read two pairs ahead, and sched_barrier keeps the compiler from
       // hoisting every read (that would need 16 more fragments live).
@@ -642,26 +714,34 @@ static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // (their blocks are many and short, and independent workgroups hide each other's barriers
   // better: measured 15% faster for 16-bit, 13-21% for e2m1 x e4m3, while dense 128-row
   // tiles gain ~10% from 8 waves and 4-wave e4m3-weight tiles spill).
-  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8) ? 8 : 4;
+  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8 || AF == A_FP4) ? 8 : 4;
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 
 template <int WP, int AF, int OF, int ST, bool ZERO>
 static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, hipStream_t st) {
   const dim3 grid(t.grid_x, t.grid_y);
-  if (moe) {
-    if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st); return true; }
-    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
+  if constexpr (AF == A_FP4) {
+    // e2m1 activations: 128-row tiles, one K slice (the other shapes spill)
+    if (t.bm != 128 || t.ksplit > 1) return false;
+    if (moe) launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st);
+    else launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st);
+    return true;
   } else {
-    if (t.ksplit > 1) {
-      if (t.bm != 128) return false;
-      launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false, true>(a, dim3(t.grid_x, t.grid_y, t.ksplit), st);
-      return true;
+    if (moe) {
+      if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st); return true; }
+      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
+    } else {
+      if (t.ksplit > 1) {
+        if (t.bm != 128) return false;
+        launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false, true>(a, dim3(t.grid_x, t.grid_y, t.ksplit), st);
+        return true;
+      }
+      if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st); return true; }
+      if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
     }
-    if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st); return true; }
-    if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
+    return false;
   }
-  return false;
 }
 
 }  // namespace qg
