@@ -203,16 +203,16 @@ static bool launch_w4a4_of(const StreamArgs& a, int bm, unsigned grid_x, unsigne
   switch (bm) {
     case 16: hipLaunchKernelGGL((w4a4_kernel<OF, MOE, 1, 2, 1, 1, 8>), grid, dim3(512), 0, st, a); return true;
     case 32: hipLaunchKernelGGL((w4a4_kernel<OF, MOE, 2, 4, 1, 1, 8>), grid, dim3(512), 0, st, a); return true;
-    case 64: hipLaunchKernelGGL((w4a4_kernel<OF, MOE, 4, 2, 1, 1, 4>), grid, dim3(256), 0, st, a); return true;
+    case 64: hipLaunchKernelGGL((w4a4_kernel<OF, MOE, 4, 4, 1, 1, 4>), grid, dim3(256), 0, st, a); return true;
     case 128: hipLaunchKernelGGL((w4a4_kernel<OF, MOE, 4, 4, 2, 2, 1>), grid, dim3(256), 0, st, a); return true;
     default: return false;
   }
 }
 
-// columns per workgroup: 32-row blocks take 64 columns (each block's activations are then
-// re-read by half as many column tiles: measured 5% faster for MoE blocks of 32), 16- and
-// 64-row workgroups 32 (more workgroups in flight: faster at M <= 16)
-int w4a4_cols(int bm) { return bm == 128 ? 128 : bm == 32 ? 64 : 32; }
+// columns per workgroup: 32- and 64-row workgroups take 64 columns (each row block's
+// activations are then re-read by half as many column tiles: 5% faster for MoE blocks of 32,
+// 31% for dense M = 128), 16-row workgroups 32 (more workgroups in flight: faster at M <= 16)
+int w4a4_cols(int bm) { return bm == 128 ? 128 : bm == 16 ? 32 : 64; }
 
 bool launch_w4a4(const StreamArgs& a, int bm, bool moe, int of, unsigned grid_y, hipStream_t st) {
   const unsigned ntiles = (unsigned)((a.n + w4a4_cols(bm) - 1) / w4a4_cols(bm));
