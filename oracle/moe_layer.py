@@ -54,6 +54,28 @@ def swiglu_e4m3(gate_up):
     return act, codes, scale
 
 
+def swiglu_mxfp4(gate_up):
+    """SwiGLU, rounded to bfloat16 (the 16-bit SwiGLU output), then MXFP4-quantized per 32-block
+    of each row (the W4A4 down product's activations).  Returns (codes uint8 [R, I/2],
+    UE8M0 bytes uint8 [R, I/32])."""
+    act = Q.round_to_bf16(swiglu(gate_up))
+    return Q.mxfp4_rows(act.reshape(-1, act.shape[-1]))
+
+
+def moe_layer_reference_mxfp4(gate_up_layer, down_layer, acts, weights) -> np.ndarray:
+    """The W4A4 layer in float64: MXFP4 activations into the gate/up product, SwiGLU rounded to
+    bfloat16 and quantized to MXFP4 between the products, then down product and combine."""
+    y1 = R.moe_reference(gate_up_layer, acts)
+    t, topk, n2 = y1.shape
+    codes, e8 = swiglu_mxfp4(np.nan_to_num(y1).reshape(t * topk, n2))
+
+    class _A:   # activation record in the storage form R.activations reads
+        x, x_scale = codes, e8
+    x2 = R.activations(_A, "e2m1").reshape(t, topk, n2 // 2)
+    y2 = down_reference(down_layer, x2, acts.topk_ids)
+    return combine(y2, weights, acts.topk_ids, down_layer.experts)
+
+
 def combine(y_slots, weights, topk_ids, experts: int) -> np.ndarray:
     """out[t, :] = sum_j w[t, j] * y[t, j, :] over slots whose expert id is in [0, E); float64 [T, N].
 

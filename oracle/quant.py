@@ -95,3 +95,16 @@ def mxfp4_rows(x):
     codes = round_to_e2m1(q).reshape(m, k)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return packed, (shared + 127).astype(np.uint8)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each finite float64 x, as float64.
+
+    bfloat16 keeps 8 significant bits: the spacing at |x| in [2^e, 2^(e+1)) is 2^(e-7), and
+    2^-133 below 2^-126 (subnormals); x / spacing is rounded half to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))             # a = f * 2^e, f in [0.5, 1)
+    spacing = np.exp2(np.maximum(e - 1, -126) - 7)
+    return np.where(a > 0, np.round(x / spacing) * spacing, x)

@@ -371,6 +371,14 @@ def moe_down_w4a8_mxfp4(experts: int = 128, n: int = 7168, k: int = 2048, seed: 
     return layer
 
 
+def moe_down_w4a4_mxfp4(experts: int = 128, n: int = 7168, k: int = 2048, seed: int = 100):
+    """Down projection of the W4A4 MXFP4 layer: MXFP4 weights drawn like moe_down_mxfp4, MXFP4
+    activations (the SwiGLU output quantized per 32-block)."""
+    layer = moe_down_mxfp4(experts=experts, n=n, k=k, seed=seed)
+    layer.name, layer.a_type = "moe_down_w4a4_mxfp4", "e2m1"
+    return layer
+
+
 def gate_up_values(rows: int, inter: int, dtype: str = "bf16", sigma: float = 4.0, seed: int = 0):
     """Gate/up rows [rows, 2*inter] as f16/bf16 bits: N(0, sigma) values plus a few exact specials
     (0, +-1, +-20, +-100) in the gate half of the first row (saturation of the sigmoid)."""

@@ -115,3 +115,41 @@ def test_mxfp4_rows_round_trips_values_on_the_grid():
     assert np.array_equal(e8.astype(np.int64) - 127, e)
     unpacked = np.stack([got & 0xF, got >> 4], axis=-1).reshape(4, 64)
     assert np.array_equal(unpacked, canon)
+
+
+def test_round_to_bf16_matches_the_cast_and_ties():
+    import torch
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.standard_normal(5000) * np.exp2(rng.integers(-40, 40, 5000)),
+                        np.exp2(-130.0) * np.arange(1, 50)])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).float().double().numpy()
+    x32 = x.astype(np.float32).astype(np.float64)            # the cast rounds float32 inputs
+    assert np.array_equal(Q.round_to_bf16(x32), ref)
+    # hand ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 (-> 1, even); 1 + 3 * 2^-8 -> 1 + 2^-6
+    assert Q.round_to_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert Q.round_to_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert Q.round_to_bf16(np.array([-(1 + 3 * 2.0 ** -8)]))[0] == -(1 + 2.0 ** -6)
+
+
+def test_w4a4_layer_reference_brute_force():
+    from oracle import moe_layer as ML
+    up, acts = synth.moe_w4a4_mxfp4(t=3, experts=2, topk=2, n=64, k=64, seed=13)
+    down = synth.moe_down_w4a4_mxfp4(experts=2, n=32, k=32, seed=14)
+    acts.topk_ids[2, 1] = -1
+    got = ML.moe_layer_reference_mxfp4(up, down, acts, acts.topk_weights)
+    for t in range(3):
+        out = np.zeros(32)
+        for j in range(2):
+            e = int(acts.topk_ids[t, j])
+            if e < 0:
+                continue
+            y1 = [sum(_VAL[_nib(acts.x[t], k)] * 2.0 ** (int(acts.x_scale[t, k // 32]) - 127) *
+                      _VAL[_nib(up.w[e, n], k)] * 2.0 ** (int(up.s[e, n, k // 32]) - 127) for k in range(64))
+                  for n in range(64)]
+            act = [y1[i] / (1 + np.exp(-y1[i])) * y1[32 + i] for i in range(32)]
+            codes, e8 = Q.mxfp4_rows(Q.round_to_bf16(np.array([act])))
+            x2 = [_VAL[_nib(codes[0], k)] * 2.0 ** (int(e8[0, k // 32]) - 127) for k in range(32)]
+            for n in range(32):
+                out[n] += float(acts.topk_weights[t, j]) * sum(
+                    x2[k] * _VAL[_nib(down.w[e, n], k)] * 2.0 ** (int(down.s[e, n, k // 32]) - 127) for k in range(32))
+        assert np.allclose(got[t], out, rtol=1e-12, atol=1e-12 * np.max(np.abs(out)))
