@@ -152,6 +152,10 @@ LAYERS = {
                            desc="MoE layer W4A8 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: per-token e4m3 "
                                 "quantization of bf16 hidden states + align + gate/up + "
                                 "SwiGLU with per-row e4m3 quantization + down + combine"),
+    "moe_w4a4_mxfp4": dict(down="moe_down_w4a4_mxfp4", hidden=7168, inter=2048, act="e2m1",
+                           desc="MoE layer W4A4 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: MXFP4 "
+                                "quantization of bf16 hidden states + align + gate/up + SwiGLU (bf16) + MXFP4 "
+                                "quantization + down + combine"),
     "moe_w4a8_int4": dict(down="moe_down_w4a8", hidden=4096, inter=1408, act="e4m3",
                           desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: per-token "
                                "e4m3 quantization of bf16 hidden states + align + gate/up + SwiGLU with per-row e4m3 "
@@ -188,13 +192,14 @@ def bench_moe_layer(args, wl):
     x_all, xs_all = layers.acts_to_dev(acts)
     # FP8-activation layers start from bf16 hidden states, quantized per token on the GPU
     # (timed as the layer's first step)
-    q_in = up.a_type == "e4m3"
+    q_in = up.a_type in ("e4m3", "e2m1")
     if q_in:
         h_bits, _ = synth.act_rows(tmax, up.k, "bf16", sigma=1.0, seed=7)
         h_all = layers.to_dev(h_bits)
     ids_all = torch.from_numpy(np.ascontiguousarray(acts.topk_ids)).cuda()
     w_all = torch.from_numpy(np.ascontiguousarray(acts.topk_weights)).cuda()
     a_e4m3 = lw["act"] == "e4m3"
+    a_e2m1 = lw["act"] == "e2m1"
     st = {}
     for t in wl["sweep"]:
         rows = t * topk
@@ -207,13 +212,16 @@ def bench_moe_layer(args, wl):
             ids=ids_all[:t].contiguous(), w=w_all[:t].contiguous(),
             y1=torch.empty((rows, 2 * lw["inter"]), dtype=torch.bfloat16, device="cuda"),
             act=torch.empty((rows, lw["inter"]), dtype=torch.uint8 if a_e4m3 else torch.bfloat16, device="cuda"),
-            asc=torch.empty(rows, dtype=torch.float32, device="cuda") if a_e4m3 else None,
+            asc=torch.empty(rows, dtype=torch.float32, device="cuda") if a_e4m3 else
+            (torch.empty((rows, lw["inter"] // 32), dtype=torch.uint8, device="cuda") if a_e2m1 else None),
+            aq=torch.empty((rows, lw["inter"] // 2), dtype=torch.uint8, device="cuda") if a_e2m1 else None,
             y2=torch.empty((rows, lw["hidden"]), dtype=torch.bfloat16, device="cuda"),
             out=torch.empty((t, lw["hidden"]), dtype=torch.bfloat16, device="cuda"),
             ws1=torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda"),
             ws2=torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda"))
     stream = torch.cuda.current_stream()
-    names = (["quant"] if q_in else []) + ["align", "gate_up", "swiglu", "down", "combine"]
+    names = ((["quant"] if q_in else []) + ["align", "gate_up", "swiglu"] + (["act_quant"] if a_e2m1 else []) +
+             ["down", "combine"])
     call = [0]
 
     def one_step(ev=None):
@@ -233,7 +241,10 @@ def bench_moe_layer(args, wl):
             mark()
             x = x_all[:t]
             if q_in:
-                qg.quantize_e4m3_rows(h_all[:t], t, up.k, qg.A_BF16, x, xs)
+                if up.a_type == "e2m1":
+                    qg.quantize_e2m1_rows(h_all[:t], t, up.k, qg.A_BF16, x, xs)
+                else:
+                    qg.quantize_e4m3_rows(h_all[:t], t, up.k, qg.A_BF16, x, xs)
                 mark()
             qg.moe_align(d["ids"], t, topk, experts, d["bm"], d["sid"], d["eid"], d["npp"])
             mark()
@@ -242,7 +253,12 @@ def bench_moe_layer(args, wl):
             qg.moe_swiglu(d["y1"], rows, lw["inter"], qg.O_BF16, qg.A_FP8_E4M3 if a_e4m3 else qg.A_BF16, d["act"],
                           d["asc"])
             mark()
-            qg.moe_gemm(h2, d["act"], d["asc"], d["sid"], d["eid"], d["npp"], rows, 1, d["bm"], d["y2"], d["ws2"])
+            a_in = d["act"]
+            if a_e2m1:
+                qg.quantize_e2m1_rows(d["act"], rows, lw["inter"], qg.A_BF16, d["aq"], d["asc"])
+                a_in = d["aq"]
+                mark()
+            qg.moe_gemm(h2, a_in, d["asc"], d["sid"], d["eid"], d["npp"], rows, 1, d["bm"], d["y2"], d["ws2"])
             mark()
             qg.moe_combine(d["y2"], d["w"], d["ids"], t, topk, experts, lw["hidden"], qg.O_BF16, d["out"])
             mark()

@@ -63,11 +63,15 @@ def swiglu_mxfp4(gate_up):
 
 
 def moe_layer_reference_mxfp4(gate_up_layer, down_layer, acts, weights) -> np.ndarray:
-    """The W4A4 layer in float64: MXFP4 activations into the gate/up product, SwiGLU rounded to
-    bfloat16 and quantized to MXFP4 between the products, then down product and combine."""
-    y1 = R.moe_reference(gate_up_layer, acts)
+    """The W4A4 layer in float64: MXFP4 activations into the gate/up product, whose output is
+    stored as bfloat16 (its declared output type, rounded to nearest even), SwiGLU rounded to
+    bfloat16 and quantized to MXFP4 between the products, then down product and combine.
+
+    Both roundings are part of the layer: the MXFP4 grid is coarse enough that leaving either
+    out moves hundreds of codes and some block exponents of a 600-row layer."""
+    y1 = Q.round_to_bf16(np.nan_to_num(R.moe_reference(gate_up_layer, acts)))
     t, topk, n2 = y1.shape
-    codes, e8 = swiglu_mxfp4(np.nan_to_num(y1).reshape(t * topk, n2))
+    codes, e8 = swiglu_mxfp4(y1.reshape(t * topk, n2))
 
     class _A:   # activation record in the storage form R.activations reads
         x, x_scale = codes, e8

@@ -272,6 +272,45 @@ def test_moe_layer_mxfp4(t):
     assert R.relative_error(got, ref) <= TOL16
 
 
+def run_layer_w4a4(up, down, acts):
+    """W4A4: align -> gate/up (MXFP4 activations) -> SwiGLU (bf16) -> MXFP4 quantization ->
+    down product (slot rows) -> combine, all on the GPU."""
+    t, topk = acts.topk_ids.shape
+    rows, inter = t * topk, down.k
+    pu, bu = layers.prepare_layer(up)
+    pd, bd = layers.prepare_layer(down)
+    bm = qg.moe_block_m(pu, t, topk)
+    assert qg.moe_block_m(pd, rows, 1) == bm
+    ids = torch.from_numpy(np.ascontiguousarray(acts.topk_ids, np.int32)).cuda()
+    s, e, n = _align(acts.topk_ids, up.experts, bm)
+    x, xs = layers.acts_to_dev(acts)
+    y1 = torch.empty((rows, 2 * inter), dtype=torch.bfloat16, device="cuda")
+    qg.moe_gemm(pu, x, xs, s, e, n, t, topk, bm, y1)
+    act = torch.empty((rows, inter), dtype=torch.bfloat16, device="cuda")
+    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_BF16, act)
+    aq = torch.empty((rows, inter // 2), dtype=torch.uint8, device="cuda")
+    asc = torch.empty((rows, inter // 32), dtype=torch.uint8, device="cuda")
+    qg.quantize_e2m1_rows(act, rows, inter, qg.A_BF16, aq, asc)
+    y2 = torch.empty((rows, down.n), dtype=torch.bfloat16, device="cuda")
+    qg.moe_gemm(pd, aq, asc, s, e, n, rows, 1, bm, y2)
+    out = torch.full((t, down.n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qg.moe_combine(y2, torch.from_numpy(acts.topk_weights).cuda(), ids, t, topk, up.experts, down.n, qg.O_BF16, out)
+    torch.cuda.synchronize()
+    return layers.out_bits_to_f64(out)
+
+
+@pytest.mark.parametrize("t", [1, 33, 300])
+def test_moe_layer_w4a4(t):
+    # both sides quantize the SwiGLU output to MXFP4; the GPU's float32 SwiGLU (fast exp) can move
+    # an element across an e2m1 midpoint, a one-step change of that element: the FP8 layers' bar
+    experts, topk, hidden, inter = 8, 2, 512, 256
+    up, acts = synth.moe_w4a4_mxfp4(t=t, experts=experts, topk=topk, n=2 * inter, k=hidden, seed=t)
+    down = synth.moe_down_w4a4_mxfp4(experts=experts, n=hidden, k=inter, seed=t + 100)
+    got = run_layer_w4a4(up, down, acts)
+    ref = ML.moe_layer_reference_mxfp4(up, down, acts, acts.topk_weights)
+    assert R.relative_error(got, ref) <= TOL8
+
+
 # ---- per-token e4m3 quantization of 16-bit activations -------------------------------------
 
 @pytest.mark.parametrize("rows,k,dtype", [(1, 8, "bf16"), (37, 1408, "bf16"), (5, 2048, "f16"), (9, 4096, "bf16"),

@@ -146,6 +146,7 @@ def test_w4a4_layer_reference_brute_force():
             y1 = [sum(_VAL[_nib(acts.x[t], k)] * 2.0 ** (int(acts.x_scale[t, k // 32]) - 127) *
                       _VAL[_nib(up.w[e, n], k)] * 2.0 ** (int(up.s[e, n, k // 32]) - 127) for k in range(64))
                   for n in range(64)]
+            y1 = Q.round_to_bf16(np.array(y1))                     # the bf16 gate/up output
             act = [y1[i] / (1 + np.exp(-y1[i])) * y1[32 + i] for i in range(32)]
             codes, e8 = Q.mxfp4_rows(Q.round_to_bf16(np.array([act])))
             x2 = [_VAL[_nib(codes[0], k)] * 2.0 ** (int(e8[0, k // 32]) - 127) for k in range(32)]
