@@ -442,8 +442,9 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
     // (activations staged through LDS, 32x32x64 fp4 MFMAs), else the W4A4 kernel
     if (!pi.binv && m > 64 && p->desc.k % 256 == 0) {
       MfmaTile t{};
-      t.bm = 128;
-      t.grid_x = (unsigned)(((m + 127) / 128) * ((p->desc.n + 255) / 256));
+      const int64_t ntiles = (p->desc.n + 255) / 256;
+      t.bm = ((m + 255) / 256) * ntiles * 2 >= 3 * kCUs ? 256 : 128;   // 256 rows: half the weight feed
+      t.grid_x = (unsigned)(((m + t.bm - 1) / t.bm) * ntiles);
       t.grid_y = 1;
       t.ksplit = 1;
       if (t.grid_x >= (unsigned)kCUs) {

@@ -503,21 +503,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
         for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = 0; }
         return A;
       };
+      // (256-row tiles read one MFMA ahead: their accumulators leave no room for a third set)
       constexpr int NQ = 4 * MT;
-      i32x8 Af4[3];
-      int sa4[3];
-      Af4[0] = read_a4(0, sa4[0]);
-      Af4[1] = read_a4(1, sa4[1]);
+      constexpr int AH = BM == 256 ? 1 : 2;      // fragments read ahead
+      i32x8 Af4[AH + 1];
+      int sa4[AH + 1];
+#pragma unroll
+      for (int q = 0; q < AH; ++q) Af4[q] = read_a4(q, sa4[q]);
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int j = q / MT, mt = q % MT;
-        if (q + 2 < NQ) Af4[(q + 2) % 3] = read_a4(q + 2, sa4[(q + 2) % 3]);
+        if (q + AH < NQ) Af4[(q + AH) % (AH + 1)] = read_a4(q + AH, sa4[(q + AH) % (AH + 1)]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           i32x8 B;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { B[i] = (int)b0[t][j][i]; B[4 + i] = 0; }
-          acc[mt][t] = mfma32x32x64_fp4_fp4(Af4[q % 3], B, sa4[q % 3],
+          acc[mt][t] = mfma32x32x64_fp4_fp4(Af4[q % (AH + 1)], B, sa4[q % (AH + 1)],
                                             (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu), acc[mt][t]);
           keep_in_vgprs(acc[mt][t]);
         }
@@ -722,11 +724,15 @@ template <int WP, int AF, int OF, int ST, bool ZERO>
 static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, hipStream_t st) {
   const dim3 grid(t.grid_x, t.grid_y);
   if constexpr (AF == A_FP4) {
-    // e2m1 activations: 128-row tiles, one K slice (the other shapes spill)
-    if (t.bm != 128 || t.ksplit > 1) return false;
-    if (moe) launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st);
-    else launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st);
-    return true;
+    // e2m1 activations: 128-row tiles (dense and MoE) and 256-row dense tiles, one K slice
+    if (t.ksplit > 1) return false;
+    if (t.bm == 128) {
+      if (moe) launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st);
+      else launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false>(a, grid, st);
+      return true;
+    }
+    if (t.bm == 256 && !moe) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, false>(a, grid, st); return true; }
+    return false;
   } else {
     if (moe) {
       if (t.bm == 128) { launch_mfma_one<WP, AF, OF, ST, ZERO, 128, true>(a, grid, st); return true; }

@@ -2,7 +2,8 @@
 both sides) and of the MXFP4 activation quantizer, through the C ABI.
 
 The product runs on the scaled fp4 x fp4 MFMA with both operands as stored: 16-, 32- and
-64-row workgroups with K split over waves, and 128 x 128 tiles.  Every product of two scaled
+64-row workgroups with K split over waves, 128 x 128 tiles, and the MFMA kernel's 128- and
+256-row tiles (activations through LDS).  Every product of two scaled
 e2m1 values is exact in float32, so the only roundings are the float32 accumulation and the
 output conversion: bar max|Y - Y_ref| / max|Y_ref| <= 2^-8 (twice the bf16 unit roundoff).
 The quantizer is compared byte for byte with the oracle's (codes and exponents).
@@ -65,6 +66,14 @@ def test_dense_128_tiles_and_f16_output():
     assert R.relative_error(_dense(layer, acts, m), R.dense_reference(layer, acts)) <= TOL
     layer, acts = synth.dense_w4a4_mxfp4(m=40, n=192, k=256, out="f16", seed=4)
     assert R.relative_error(_dense(layer, acts, 40), R.dense_reference(layer, acts)) <= TOL
+
+
+def test_dense_256_row_mfma_tiles():
+    # enough 256 x 256 tiles (17 x 24) for the 256-row fp4 MFMA tiles, a ragged last row tile;
+    # K = 512: two 256-wide steps
+    m, n, k = 4100, 6144, 512
+    layer, acts = synth.dense_w4a4_mxfp4(m=m, n=n, k=k, seed=21)
+    assert R.relative_error(_dense(layer, acts, m), R.dense_reference(layer, acts)) <= TOL
 
 
 def test_batch_invariant_rows_are_bitwise_equal():
