@@ -154,8 +154,8 @@ LAYERS = {
                                 "SwiGLU with per-row e4m3 quantization + down + combine"),
     "moe_w4a4_mxfp4": dict(down="moe_down_w4a4_mxfp4", hidden=7168, inter=2048, act="e2m1",
                            desc="MoE layer W4A4 MXFP4, E=128 top-8, hidden 7168, intermediate 2048: MXFP4 "
-                                "quantization of bf16 hidden states + align + gate/up + SwiGLU (bf16) + MXFP4 "
-                                "quantization + down + combine"),
+                                "quantization of bf16 hidden states + align + gate/up + SwiGLU with MXFP4 output "
+                                "+ down + combine"),
     "moe_w4a8_int4": dict(down="moe_down_w4a8", hidden=4096, inter=1408, act="e4m3",
                           desc="MoE layer W4A8 int4, E=64 top-6 skewed, hidden 4096, intermediate 1408: per-token "
                                "e4m3 quantization of bf16 hidden states + align + gate/up + SwiGLU with per-row e4m3 "
@@ -211,7 +211,8 @@ def bench_moe_layer(args, wl):
             eid=torch.empty(cb, dtype=torch.int32, device="cuda"), npp=torch.empty(1, dtype=torch.int32, device="cuda"),
             ids=ids_all[:t].contiguous(), w=w_all[:t].contiguous(),
             y1=torch.empty((rows, 2 * lw["inter"]), dtype=torch.bfloat16, device="cuda"),
-            act=torch.empty((rows, lw["inter"]), dtype=torch.uint8 if a_e4m3 else torch.bfloat16, device="cuda"),
+            act=None if a_e2m1 else
+            torch.empty((rows, lw["inter"]), dtype=torch.uint8 if a_e4m3 else torch.bfloat16, device="cuda"),
             asc=torch.empty(rows, dtype=torch.float32, device="cuda") if a_e4m3 else
             (torch.empty((rows, lw["inter"] // 32), dtype=torch.uint8, device="cuda") if a_e2m1 else None),
             aq=torch.empty((rows, lw["inter"] // 2), dtype=torch.uint8, device="cuda") if a_e2m1 else None,
@@ -220,8 +221,7 @@ def bench_moe_layer(args, wl):
             ws1=torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda"),
             ws2=torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda"))
     stream = torch.cuda.current_stream()
-    names = ((["quant"] if q_in else []) + ["align", "gate_up", "swiglu"] + (["act_quant"] if a_e2m1 else []) +
-             ["down", "combine"])
+    names = (["quant"] if q_in else []) + ["align", "gate_up", "swiglu", "down", "combine"]
     call = [0]
 
     def one_step(ev=None):
@@ -250,14 +250,10 @@ def bench_moe_layer(args, wl):
             mark()
             qg.moe_gemm(h1, x, xs, d["sid"], d["eid"], d["npp"], t, topk, d["bm"], d["y1"], d["ws1"])
             mark()
-            qg.moe_swiglu(d["y1"], rows, lw["inter"], qg.O_BF16, qg.A_FP8_E4M3 if a_e4m3 else qg.A_BF16, d["act"],
-                          d["asc"])
+            a_in = d["aq"] if a_e2m1 else d["act"]
+            qg.moe_swiglu(d["y1"], rows, lw["inter"], qg.O_BF16,
+                          qg.A_FP8_E4M3 if a_e4m3 else qg.A_FP4_E2M1 if a_e2m1 else qg.A_BF16, a_in, d["asc"])
             mark()
-            a_in = d["act"]
-            if a_e2m1:
-                qg.quantize_e2m1_rows(d["act"], rows, lw["inter"], qg.A_BF16, d["aq"], d["asc"])
-                a_in = d["aq"]
-                mark()
             qg.moe_gemm(h2, a_in, d["asc"], d["sid"], d["eid"], d["npp"], rows, 1, d["bm"], d["y2"], d["ws2"])
             mark()
             qg.moe_combine(d["y2"], d["w"], d["ids"], t, topk, experts, lw["hidden"], qg.O_BF16, d["out"])

@@ -278,12 +278,17 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, 
  *             out_scale[r] = max_i |act[r][i]| / 448 (float32; 1 for an all-zero row) and
  *             out (uint8 [rows][inter]) = e4m3 codes, round to nearest even of
  *             clamp(act / out_scale[r], -448, 448)
- *   out_scale device float32 [rows] for QG_A_FP8_E4M3, else ignored (may be NULL)
- * inter % 8 == 0 (and inter <= 8192 for QG_A_FP8_E4M3), else QG_ERR_UNSUPPORTED.  Rows of
+ *             QG_A_FP4_E2M1: each row quantized for the next product's MXFP4 activations: act
+ *             rounded to bfloat16 (nearest even), then exactly qg_quantize_e2m1_rows of those
+ *             rows; out = packed e2m1 codes uint8 [rows][inter/2] (16-byte aligned)
+ *   out_scale device float32 [rows] for QG_A_FP8_E4M3, uint8 [rows][inter/32] UE8M0 exponents
+ *             for QG_A_FP4_E2M1, else ignored (may be NULL)
+ * inter % 8 == 0 (and inter <= 8192 for QG_A_FP8_E4M3, inter % 32 == 0 for QG_A_FP4_E2M1),
+ * else QG_ERR_UNSUPPORTED.  Rows of
  * slots the gate/up product did not write give unspecified values, which nothing reads.
  */
 qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_t in_type, int32_t out_type,
-                        void* out, float* out_scale, void* stream);
+                        void* out, void* out_scale, void* stream);
 
 /*
  * qg_quantize_e4m3_rows: per-token FP8 quantization of 16-bit activations, the input of the

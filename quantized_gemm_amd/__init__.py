@@ -185,7 +185,7 @@ def moe_gemm(p: Prepared, x, x_scale, sorted_ids, expert_ids, num_post_pad, toke
 
 
 def moe_swiglu(gate_up, rows: int, inter: int, in_type: int, out_type: int, out, out_scale=None, stream=None):
-    """act = silu(gate) * up per row (gate = first ``inter`` columns); f16/bf16 or per-row e4m3 output."""
+    """act = silu(gate) * up per row (gate = first ``inter`` columns); f16/bf16, per-row e4m3 or MXFP4 output."""
     st = lib().qg_moe_swiglu(_ptr(gate_up), rows, inter, in_type, out_type, _ptr(out), _ptr(out_scale),
                              _stream(stream))
     _check(st, "qg_moe_swiglu")

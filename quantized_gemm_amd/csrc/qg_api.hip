@@ -682,22 +682,26 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, 
 }
 
 qg_status qg_moe_swiglu(const void* gate_up, int64_t rows, int64_t inter, int32_t in_type, int32_t out_type, void* out,
-                        float* out_scale, void* stream) {
+                        void* out_scale, void* stream) {
   if (rows < 0 || inter <= 0) return QG_ERR_INVALID_ARG;
   if (in_type != QG_O_F16 && in_type != QG_O_BF16) return QG_ERR_INVALID_ARG;
-  if (out_type != QG_A_F16 && out_type != QG_A_BF16 && out_type != QG_A_FP8_E4M3) return QG_ERR_INVALID_ARG;
+  if (out_type != QG_A_F16 && out_type != QG_A_BF16 && out_type != QG_A_FP8_E4M3 && out_type != QG_A_FP4_E2M1)
+    return QG_ERR_INVALID_ARG;
   if (inter % 8 != 0) return QG_ERR_UNSUPPORTED;
   if (out_type == QG_A_FP8_E4M3 && inter > 8192) return QG_ERR_UNSUPPORTED;
+  if (out_type == QG_A_FP4_E2M1 && inter % 32 != 0) return QG_ERR_UNSUPPORTED;
   if (rows > ((int64_t)1 << 31) - 1 || rows * inter > ((int64_t)1 << 40)) return QG_ERR_UNSUPPORTED;
   if (rows == 0) return QG_OK;
   if (!gate_up || !out || !aligned16(gate_up) || !aligned16(out)) return QG_ERR_INVALID_ARG;
   if (out_type == QG_A_FP8_E4M3 && (!out_scale || ((uintptr_t)out_scale & 3u) != 0)) return QG_ERR_INVALID_ARG;
+  if (out_type == QG_A_FP4_E2M1 && !out_scale) return QG_ERR_INVALID_ARG;
   qg_status s = check_arch();
   if (s != QG_OK) return s;
   const int in_t = in_type == QG_O_F16 ? O_F16 : O_BF16;
-  const int out_t = out_type == QG_A_FP8_E4M3 ? A_FP8 : (out_type == QG_A_F16 ? A_F16 : A_BF16);
-  if (!launch_swiglu(gate_up, rows, inter, in_t, out_t, out, out_type == QG_A_FP8_E4M3 ? out_scale : nullptr,
-                     (hipStream_t)stream))
+  const int out_t = out_type == QG_A_FP8_E4M3 ? A_FP8
+                    : out_type == QG_A_FP4_E2M1 ? A_FP4 : (out_type == QG_A_F16 ? A_F16 : A_BF16);
+  const bool scaled = out_type == QG_A_FP8_E4M3 || out_type == QG_A_FP4_E2M1;
+  if (!launch_swiglu(gate_up, rows, inter, in_t, out_t, out, scaled ? out_scale : nullptr, (hipStream_t)stream))
     return QG_ERR_UNSUPPORTED;
   return launched();
 }

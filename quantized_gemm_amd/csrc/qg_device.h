@@ -187,6 +187,35 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8_fp4(i32x8 a, i32x8 b, int sb,
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
 }
 
+// MXFP4 encoding of 32 finite values (the OCP Microscaling conversion): shared exponent
+// E = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for an all-zero block), codes = the
+// e2m1 value nearest to v / 2^E, ties to the even code, magnitudes above 6 giving 6, negative
+// only when not zero.  The scaling by 2^-E is exact and each comparison is against an e2m1
+// midpoint, so no rounding enters.  Returns the UE8M0 byte E + 127; codes packed 8 per word,
+// element 2j in the low nibble of byte j.
+__device__ __forceinline__ uint32_t mxfp4_encode32(const float* v, u32x4& packed) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // amax = f * 2^e with f in [0.5, 1): floor(log2 amax) = e - 1
+  const int e = amax > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(amax) - 3)) : -127;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const float q = __builtin_ldexpf(v[8 * j + h], -e);
+      const float m = fabsf(q);
+      uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
+                   (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+      if (q < 0.f && c != 0) c |= 8u;
+      word |= c << (4 * h);
+    }
+    packed[j] = word;
+  }
+  return (uint32_t)(e + 127);
+}
+
 // e2m1 x e2m1 with E8M0 block exponents for both operands (format code 4 for A and B)
 __device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp4(i32x8 a, i32x8 b, int sa, int sb, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);

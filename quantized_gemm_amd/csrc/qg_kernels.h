@@ -73,8 +73,9 @@ struct DequantArgs {
 void launch_dequant(const DequantArgs& a, hipStream_t st);
 
 // MoE layer steps around the grouped products (qg_moe_layer.hip).  in_t / dtype: O_F16 or
-// O_BF16; out_t: A_F16, A_BF16 or A_FP8 (then out_scale receives one scale per row).
-bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, float* out_scale,
+// O_BF16; out_t: A_F16, A_BF16, A_FP8 (out_scale: float32, one scale per row) or A_FP4
+// (out: packed e2m1 codes, out_scale: uint8 UE8M0 exponent per 32 outputs).
+bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, void* out_scale,
                    hipStream_t st);
 // Per-row absmax e4m3 quantization of 16-bit rows (in_t O_F16 / O_BF16), k <= 8192, k % 8 == 0.
 bool launch_quant_rows_e4m3(const void* x, int64_t rows, int64_t k, int in_t, void* codes, float* scale,

@@ -71,6 +71,27 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
   *(u32x4*)(out + r * inter + 8 * c8) = pack8<OUT>(act);
 }
 
+// SwiGLU -> MXFP4, one thread per 32 outputs of a row: the activations are computed exactly as
+// swiglu_kernel does, rounded to bfloat16 (the 16-bit SwiGLU output), then encoded, so the
+// result equals swiglu_kernel followed by the MXFP4 row quantizer bit for bit.
+template <int IN>
+__global__ __launch_bounds__(256) void swiglu_e2m1_kernel(const uint16_t* __restrict__ gu, int64_t rows, int64_t inter,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t per_row = inter >> 5;
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= rows * per_row) return;
+  const int64_t r = p / per_row, blk = p - r * per_row;
+  float act[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) swiglu8<IN>(gu + r * 2 * inter, inter, 4 * blk + q, act + 8 * q);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) act[i] = bf16_bits_to_f32(f32_to_out<O_BF16>(act[i]));
+  u32x4 packed;
+  const uint32_t e8 = mxfp4_encode32(act, packed);
+  *(u32x4*)(codes + r * (inter >> 1) + 16 * blk) = packed;
+  scales[p] = (uint8_t)e8;
+}
+
 // One workgroup of 256 threads per row; each thread keeps up to kSwigluE4m3Pieces pieces of 8
 // activations in registers while the row's absmax is reduced, then quantizes them.
 constexpr int kSwigluE4m3Pieces = 4;   // inter <= 256 * 4 * 8 = 8192
@@ -235,10 +256,19 @@ static bool launch_rows_e4m3(const uint16_t* g, int64_t rows, int64_t inter, int
   return true;
 }
 
-bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, float* out_scale,
+bool launch_swiglu(const void* gu, int64_t rows, int64_t inter, int in_t, int out_t, void* out, void* out_scale,
                    hipStream_t st) {
   const uint16_t* g = (const uint16_t*)gu;
-  if (out_t == A_FP8) return launch_rows_e4m3<true>(g, rows, inter, in_t, out, out_scale, st);
+  if (out_t == A_FP8) return launch_rows_e4m3<true>(g, rows, inter, in_t, out, (float*)out_scale, st);
+  if (out_t == A_FP4) {
+    const dim3 grid4((unsigned)((rows * (inter >> 5) + 255) / 256));
+    uint8_t* c = (uint8_t*)out;
+    uint8_t* e = (uint8_t*)out_scale;
+    if (in_t == O_BF16) hipLaunchKernelGGL((swiglu_e2m1_kernel<O_BF16>), grid4, dim3(256), 0, st, g, rows, inter, c, e);
+    else if (in_t == O_F16) hipLaunchKernelGGL((swiglu_e2m1_kernel<O_F16>), grid4, dim3(256), 0, st, g, rows, inter, c, e);
+    else return false;
+    return true;
+  }
   const int64_t pieces = rows * (inter >> 3);
   const dim3 grid((unsigned)((pieces + 255) / 256));
   uint16_t* o = (uint16_t*)out;

@@ -226,11 +226,7 @@ bool launch_w4a4(const StreamArgs& a, int bm, bool moe, int of, unsigned grid_y,
 }
 
 // ---- MXFP4 activation quantization -----------------------------------------------------
-// One thread per 32-element block of a row: shared exponent E = floor(log2 amax) - 2
-// clamped to [-127, 127] (byte 0 for an all-zero block), codes = nearest e2m1 value of
-// x / 2^E with ties to the even code and saturation at 6, negative only when not zero
-// (the OCP Microscaling conversion; the scaling by 2^-E is exact, and every comparison is
-// against a value on the e2m1 midpoint grid, so no rounding enters).
+// One thread per 32-element block of a row (mxfp4_encode32: the OCP Microscaling conversion).
 template <int IN>
 __global__ __launch_bounds__(256) void quant_e2m1_rows_kernel(const uint16_t* x, int64_t blocks, int kg,
                                                                uint8_t* codes, uint8_t* scales) {
@@ -249,28 +245,10 @@ __global__ __launch_bounds__(256) void quant_e2m1_rows_kernel(const uint16_t* x,
       v[8 * p + 2 * j + 1] = IN == A_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // amax = f * 2^e with f in [0.5, 1): floor(log2 amax) = e - 1
-  const int e = amax > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(amax) - 3)) : -127;
   u32x4 out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const float q = __builtin_ldexpf(v[8 * j + h], -e);
-      const float m = fabsf(q);
-      uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) + (uint32_t)(m >= 1.75f) +
-                   (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
-      if (q < 0.f && c != 0) c |= 8u;
-      word |= c << (4 * h);
-    }
-    out[j] = word;
-  }
+  const uint32_t e8 = mxfp4_encode32(v, out);
   *(u32x4*)(codes + row * (int64_t)kg * 16 + blk * 16) = out;
-  scales[b] = (uint8_t)(e + 127);
+  scales[b] = (uint8_t)e8;
 }
 
 bool launch_quant_rows_e2m1(const void* x, int64_t rows, int64_t k, int in_t, uint8_t* codes, uint8_t* scales,

@@ -141,6 +141,8 @@ def test_moe_layer_steps_reject_on_the_host():
     assert lib.qg_moe_swiglu(None, 4, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
     assert lib.qg_moe_swiglu(ctypes.c_void_p(4104), 4, 64, qg.O_BF16, qg.A_BF16, fake, None, None) == 1
     assert lib.qg_moe_swiglu(fake, 4, 64, qg.O_BF16, qg.A_FP8_E4M3, fake, None, None) == 1   # scales missing
+    assert lib.qg_moe_swiglu(fake, 4, 64, qg.O_BF16, qg.A_FP4_E2M1, fake, None, None) == 1   # exponents missing
+    assert lib.qg_moe_swiglu(fake, 4, 48, qg.O_BF16, qg.A_FP4_E2M1, fake, fake, None) == 2   # inter % 32
     # combine: (y, weights, ids, tokens, topk, experts, n, dtype, out, stream)
     assert lib.qg_moe_combine(fake, fake, fake, 0, 2, 8, 64, qg.O_BF16, fake, None) == 0
     assert lib.qg_moe_combine(fake, fake, fake, 4, 0, 8, 64, qg.O_BF16, fake, None) == 1

@@ -90,6 +90,53 @@ def test_swiglu_e4m3_is_bit_exact_on_exact_activations(rows, inter):
     assert np.array_equal(codes, rc), f"{np.count_nonzero(codes != rc)} codes differ"
 
 
+def _swiglu_e2m1_gpu(gu, rows, inter, din):
+    codes = torch.full((rows, inter // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    e8 = torch.full((rows, inter // 32), 0xCD, dtype=torch.uint8, device="cuda")
+    qg.moe_swiglu(_dev16(gu), rows, inter, Q_OUT[din], qg.A_FP4_E2M1, codes, e8)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), e8.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,inter,din", [(6, 64, "bf16"), (11, 1408, "bf16"), (3, 2048, "f16")])
+def test_swiglu_e2m1_is_bit_exact_on_exact_activations(rows, inter, din):
+    # gates in {0, 32, 64, 128}: silu(g) is g in float32 (sigmoid rounds to 1) and rounds to g
+    # from float64, so act = g * up is exact on both sides and the bfloat16 rounding and the
+    # MXFP4 decisions must agree bit for bit (an all-zero block included)
+    rng = np.random.default_rng(inter + rows)
+    v = synth.gate_up_values(rows, inter, din, seed=inter).copy()
+    gates = np.array([0.0, 32.0, 64.0, 128.0], np.float32)[rng.integers(0, 4, size=(rows, inter))]
+    v[:, :inter] = synth.f32_to_bf16_bits(gates) if din == "bf16" else synth.f32_to_f16_bits(gates)
+    if din == "f16":
+        # f16 up values have 11 significant bits: g * up could then sit exactly on a bfloat16
+        # tie, which the exact float32 product rounds to even and float64 (silu(g) = g (1 - eps))
+        # rounds down.  Up values with 8 significant bits keep g * up itself a bfloat16 value.
+        up = F.decode_f16(v[:, inter:]).astype(np.float32)
+        up = F.decode_bf16(synth.f32_to_bf16_bits(up)).astype(np.float32)
+        v[:, inter:] = synth.f32_to_f16_bits(up)
+    v[0, :32] = v[0, :32] * 0                               # gate 0 on a whole block: zeros
+    codes, e8 = _swiglu_e2m1_gpu(v, rows, inter, din)
+    rc, re8 = ML.swiglu_mxfp4(_bits_to_f64(v, din))
+    assert np.array_equal(e8, re8)
+    assert np.array_equal(codes, rc), f"{np.count_nonzero(codes != rc)} code bytes differ"
+
+
+@pytest.mark.parametrize("rows,inter,din", [(40, 1408, "bf16"), (7, 2048, "f16")])
+def test_swiglu_e2m1_equals_swiglu_then_quantizer(rows, inter, din):
+    # the fused output is defined as the 16-bit SwiGLU rounded to bfloat16 and then the MXFP4
+    # row quantizer: both routes on the GPU must give the same bytes (the values themselves are
+    # checked against the oracle above and in the layer test)
+    gu = synth.gate_up_values(rows, inter, din, seed=5 * rows + inter)
+    codes, e8 = _swiglu_e2m1_gpu(gu, rows, inter, din)
+    act = torch.empty((rows, inter), dtype=torch.bfloat16, device="cuda")
+    qg.moe_swiglu(_dev16(gu), rows, inter, Q_OUT[din], qg.A_BF16, act)
+    c2 = torch.empty((rows, inter // 2), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((rows, inter // 32), dtype=torch.uint8, device="cuda")
+    qg.quantize_e2m1_rows(act, rows, inter, qg.A_BF16, c2, s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes, c2.cpu().numpy()) and np.array_equal(e8, s2.cpu().numpy())
+
+
 @pytest.mark.parametrize("rows,inter,din", [(40, 1408, "bf16"), (7, 2048, "f16"), (2, 8, "bf16")])
 def test_swiglu_e4m3_general(rows, inter, din):
     gu = synth.gate_up_values(rows, inter, din, seed=3 * rows + inter)
@@ -273,8 +320,8 @@ def test_moe_layer_mxfp4(t):
 
 
 def run_layer_w4a4(up, down, acts):
-    """W4A4: align -> gate/up (MXFP4 activations) -> SwiGLU (bf16) -> MXFP4 quantization ->
-    down product (slot rows) -> combine, all on the GPU."""
+    """W4A4: align -> gate/up (MXFP4 activations) -> SwiGLU with MXFP4 output -> down product
+    (slot rows) -> combine, all on the GPU."""
     t, topk = acts.topk_ids.shape
     rows, inter = t * topk, down.k
     pu, bu = layers.prepare_layer(up)
@@ -286,11 +333,9 @@ def run_layer_w4a4(up, down, acts):
     x, xs = layers.acts_to_dev(acts)
     y1 = torch.empty((rows, 2 * inter), dtype=torch.bfloat16, device="cuda")
     qg.moe_gemm(pu, x, xs, s, e, n, t, topk, bm, y1)
-    act = torch.empty((rows, inter), dtype=torch.bfloat16, device="cuda")
-    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_BF16, act)
     aq = torch.empty((rows, inter // 2), dtype=torch.uint8, device="cuda")
     asc = torch.empty((rows, inter // 32), dtype=torch.uint8, device="cuda")
-    qg.quantize_e2m1_rows(act, rows, inter, qg.A_BF16, aq, asc)
+    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_FP4_E2M1, aq, asc)   # SwiGLU -> bf16 -> MXFP4
     y2 = torch.empty((rows, down.n), dtype=torch.bfloat16, device="cuda")
     qg.moe_gemm(pd, aq, asc, s, e, n, rows, 1, bm, y2)
     out = torch.full((t, down.n), float("nan"), dtype=torch.bfloat16, device="cuda")
