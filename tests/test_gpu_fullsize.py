@@ -142,10 +142,14 @@ def _layer_gpu(up, down, acts, t, act_type):
     y1 = torch.empty((rows, 2 * inter), dtype=torch.bfloat16, device="cuda")
     ws1 = torch.zeros(max(1, qg.workspace_bytes(pu, t, topk)), dtype=torch.uint8, device="cuda")
     qg.moe_gemm(pu, x, xs, sid, eid, npp, t, topk, bm, y1, ws1)
-    e4 = act_type == "e4m3"
-    act = torch.empty((rows, inter), dtype=torch.uint8 if e4 else torch.bfloat16, device="cuda")
-    asc = torch.empty(rows, dtype=torch.float32, device="cuda") if e4 else None
-    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_FP8_E4M3 if e4 else qg.A_BF16, act, asc)
+    e4, f4 = act_type == "e4m3", act_type == "e2m1"
+    if f4:   # SwiGLU -> bf16 -> MXFP4 codes [rows][inter/2] and exponents [rows][inter/32]
+        act = torch.empty((rows, inter // 2), dtype=torch.uint8, device="cuda")
+        asc = torch.empty((rows, inter // 32), dtype=torch.uint8, device="cuda")
+    else:
+        act = torch.empty((rows, inter), dtype=torch.uint8 if e4 else torch.bfloat16, device="cuda")
+        asc = torch.empty(rows, dtype=torch.float32, device="cuda") if e4 else None
+    qg.moe_swiglu(y1, rows, inter, qg.O_BF16, qg.A_FP8_E4M3 if e4 else qg.A_FP4_E2M1 if f4 else qg.A_BF16, act, asc)
     y2 = torch.empty((rows, down.n), dtype=torch.bfloat16, device="cuda")
     ws2 = torch.zeros(max(1, qg.workspace_bytes(pd, rows, 1)), dtype=torch.uint8, device="cuda")
     qg.moe_gemm(pd, act, asc, sid, eid, npp, rows, 1, bm, y2, ws2)
@@ -183,6 +187,39 @@ def test_moe_layer_mxfp4_e128_full_size(c4_layer, t):
             ref[i] += float(acts.topk_weights[tk, j]) * R.dense_gemm(a, R.dequant_rows(down, e, cols))[0]
     err = R.relative_error(got, ref)
     assert err <= TOL16, f"T={t}: relative error {err:.3g}"
+
+
+@pytest.fixture(scope="module")
+def c4_layer_w4a4():
+    up, acts = synth.moe_w4a4_mxfp4(t=4096, experts=128, topk=8, n=4096, k=7168, seed=0)
+    down = synth.moe_down_w4a4_mxfp4(experts=128, n=7168, k=2048, seed=100)
+    return up, down, acts
+
+
+@pytest.mark.parametrize("t", [16, 4096])
+def test_moe_layer_w4a4_e128_full_size(c4_layer_w4a4, t):
+    # W4A4 at the MXFP4 layer's shapes: each sampled token's gate/up rows in full (rounded to
+    # bfloat16, the product's output type), SwiGLU -> bfloat16 -> MXFP4 in the oracle, then the
+    # sampled columns of the down product; the FP8 layers' bar (requantization can move a code)
+    from oracle import moe_layer as ML
+    from oracle import quant as Q
+    up, down, acts = c4_layer_w4a4
+    out = _layer_gpu(up, down, acts, t, "e2m1")
+    rng = np.random.default_rng(t + 7)
+    toks = np.unique(np.array([0, t - 1, int(rng.integers(0, t))]))
+    cols = _sample(rng, down.n, N_COLS)
+    got = layers.out_bits_to_f64(out[torch.from_numpy(toks).cuda()][:, torch.from_numpy(cols).cuda()])
+    x = R.activations(synth.Acts(acts.x[toks], acts.x_scale[toks], None), "e2m1")
+    ref = np.zeros((toks.size, cols.size))
+    for i, tk in enumerate(toks):
+        for j in range(acts.topk_ids.shape[1]):
+            e = int(acts.topk_ids[tk, j])
+            h = Q.round_to_bf16(R.dense_gemm(x[i:i + 1], R.dequant_layer(up, e)))
+            codes, e8 = ML.swiglu_mxfp4(h)
+            a = R.activations(synth.Acts(codes, e8, None), "e2m1")
+            ref[i] += float(acts.topk_weights[tk, j]) * R.dense_gemm(a, R.dequant_rows(down, e, cols))[0]
+    err = R.relative_error(got, ref)
+    assert err <= TOL8, f"T={t}: relative error {err:.3g}"
 
 
 @pytest.mark.parametrize("t", [64, 8192])
