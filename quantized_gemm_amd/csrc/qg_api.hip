@@ -399,9 +399,10 @@ static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
   a.z_bytes = (uint32_t)(p->z_expert_bytes * p->desc.num_experts);
 }
 
-// W4A4 rows per workgroup for a dense product: 16 / 32 / 64-row workgroups (K split over 8
-// waves) while the 128 x 128 tiles would leave the GPU under-filled, 128 x 128 tiles above;
-// batch-invariant: 128 x 128 tiles for every M (each output then one wave's full K loop).
+// W4A4 rows per workgroup of the W4A4 kernel for a dense product: 16 / 32 / 64-row workgroups
+// (K split over 8, 8 and 4 waves) while 128 x 128 tiles would leave the GPU under-filled,
+// 128 x 128 tiles above; batch-invariant: 128 x 128 tiles for every M (each output then one
+// wave's full K loop).  Larger products go to the MFMA kernel before this is asked.
 int w4a4_dense_rows(int64_t m, int64_t n, bool binv) {
   if (binv) return 128;
   if (m <= 16) return 16;

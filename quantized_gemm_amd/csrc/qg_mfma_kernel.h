@@ -10,7 +10,10 @@
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
 //     in the epilogue;
 //   * e4m3 x e2m1 (W4A8 MXFP4): no dequantization at all, the e2m1 codes and their UE8M0
-//     block scales are operands of the scaled fp8/fp4 MFMA; per-token scale in the epilogue.
+//     block scales are operands of the scaled fp8/fp4 MFMA; per-token scale in the epilogue;
+//   * e2m1 x e2m1 (W4A4 MXFP4): both operands and both UE8M0 exponents go to the scaled
+//     fp4 x fp4 MFMA; a 128-byte row segment holds 256 K, and each step's activation
+//     exponents travel into LDS with the step's activations.
 //
 // Tile: BM x 256 per workgroup, CW waves, wave w owning all BM rows of the columns
 // [w 256/CW, (w+1) 256/CW), so that every weight is dequantized exactly once per tile.

@@ -10,6 +10,8 @@
 // the low nibble, and supplies the exponent of that 32-wide block.  That is 16 contiguous
 // bytes of a packed activation row, and one 16-byte unit of the prepared weights.
 //
+// Used for up to 64 rows, mid M and MoE blocks up to 64, and for batch invariance; larger
+// products run on the MFMA kernel (activations staged through LDS).
 // Workgroup: KW x WC x WR waves.  Wave (wr, wc, kw) owns rows [16 MT wr, +16 MT) and columns
 // [16 NT wc, +16 NT) of the workgroup tile and the K chunks kw, kw + KW, ...; with KW > 1
 // the waves' partial sums are added in LDS in wave order (a fixed order), then written by
