@@ -123,8 +123,19 @@ def test_moe_selected_block(t):
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL, f"block {bm}"
 
 
+def test_moe_mfma_block_with_dropped_slot():
+    # K = 768 (three 256-wide steps): 128-row blocks run on the MFMA kernel
+    layer, acts = synth.moe_w4a4_mxfp4(t=300, experts=4, topk=2, n=320, k=768, seed=129)
+    acts.topk_ids[5, 0] = -1
+    _, y = _moe(layer, acts, 128)
+    ref = R.moe_reference(layer, acts)
+    assert np.all(np.isnan(y[5, 0]))
+    ok = ~np.isnan(ref[:, :, 0])
+    assert R.relative_error(y[ok], ref[ok]) <= TOL
+
+
 def test_block_sizes_outside_the_kernel_are_rejected():
-    layer, acts = synth.moe_w4a4_mxfp4(t=8, experts=4, topk=2, n=128, k=256, seed=2)
+    layer, acts = synth.moe_w4a4_mxfp4(t=8, experts=4, topk=2, n=128, k=384, seed=2)
     with pytest.raises(qg.QGError):
         _moe(layer, acts, 4)
     with pytest.raises(qg.QGError):
