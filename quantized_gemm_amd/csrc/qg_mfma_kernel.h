@@ -492,7 +492,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
     };
     if constexpr (F8) pin_scales();
 
-    if constexpr (F4A) {
+    // Byte-operand paths issue all of a step's loads above, so a padded step (past the end of
+    // K) can skip its MFMAs, which would only add zeros; the 16-bit path interleaves its
+    // activation loads with the MFMAs and runs padded steps in full.
+    if (F8 && step >= nsteps) {
+    } else if constexpr (F4A) {
       // 4 x MT MFMAs per step (K quarters j, row tiles mt), 32x32x64 with both operands e2m1:
       // lane (r, g) gives row r's K 64j + 32g .. + 31 (16 bytes, chunk 2j + g of the row
       // segment) and its exponent; fragments are read two MFMAs ahead as in the e4m3 loop
