@@ -69,6 +69,81 @@ WORKLOADS = {
 }
 
 
+DEFAULT_WORKLOAD = "dense_w4a16_asym_bf16"
+# The other benchmark workloads the default line carries (each its own sweep and roofline).
+EXTRA_WORKLOADS = ["dense_w4a16_sym_f16", "dense_w8a8_fp8", "moe_w4a16_mxfp4", "moe_w4a8_int4"]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measure_ceilings(args):
+    """Measured ceilings of this GPU: a streaming read of cold buffers the size of the dense
+    W4A16 layer's weight stream (34 865 152 bytes), rotated over >= 1 GiB so every launch
+    reads from HBM, and of 256 MiB buffers; back-to-back MFMAs of each arithmetic type."""
+    import torch
+    import quantized_gemm_amd as qg
+    stream = torch.cuda.current_stream()
+    out = {"read_us": {}, "read_GBps_by_loads_per_lane": {}}
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    reps = max(20, args.steps)
+    for size, label in ((34865152, "weights_34.9MB"), (256 << 20, "256MiB")):
+        stride = (size + 4095) // 4096 * 4096
+        nbuf = (1 << 30) // stride
+        best = None
+        for u in (2, 4, 8, 16):
+            def launch(i):
+                qg.ceiling_read(pool[(i % nbuf) * stride:], size, u, sink)
+            for i in range(3):
+                launch(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            gbps = size / (us * 1e-6) / 1e9
+            out["read_GBps_by_loads_per_lane"][f"{label}_u{u}"] = round(gbps, 1)
+            if best is None or us < best[0]:
+                best = (us, gbps, u)
+        out["read_us"][label] = round(best[0], 2)
+        out[f"read_GBps_{label}"] = round(best[1], 1)
+    out["read_GBps"] = out["read_GBps_weights_34.9MB"]
+    del pool
+    flop_per = {0: 32768, 1: 131072, 2: 131072}
+    names = {0: "bf16", 1: "fp8", 2: "fp4"}
+    out["mfma_tflops"] = {}
+    wgs, iters = 512, 4000
+    msink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    for dt in (0, 1, 2):
+        qg.ceiling_mfma(dt, 100, wgs, msink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        qg.ceiling_mfma(dt, iters, wgs, msink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3
+        out["mfma_tflops"][names[dt]] = round(wgs * 4 * iters * 4 * flop_per[dt] / s / 1e12, 1)
+    out["mfma_tflops"]["f16"] = out["mfma_tflops"]["bf16"]
+    out["method"] = ("read: qg_ceiling_read, best of 2/4/8/16 16-byte loads per lane, back-to-back launches "
+                     "between HIP events over buffers rotated through 1 GiB; mfma: qg_ceiling_mfma, 512 "
+                     "workgroups x 4 waves x 4 independent 32x32 MFMAs per iteration")
+    return out
+
+
 def weight_bytes(layer):
     """Algorithmic weight bytes of ONE expert: packed codes + scales + zero points (4-bit packed)."""
     bits = 8 if layer.w_type == "e4m3" else 4
@@ -137,7 +212,7 @@ def cpu_baseline(builder, wl, budget_cols):
     except Exception:
         pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"float64 dequant + numpy.matmul of the first {budget_cols} of {layer.n} output columns, "
                       f"every M of the sweep {wl['sweep']}"}
 
@@ -305,43 +380,15 @@ def bench_moe_layer(args, wl):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense_w4a16_asym_bf16", choices=list(WORKLOADS))
-    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-cols", type=int, default=8192)
-    ap.add_argument("--sweep", type=str, default="", help="comma-separated M values overriding the workload's sweep")
-    ap.add_argument("--layer", action="store_true",
-                    help="MoE workloads: time the whole layer (align, gate/up, SwiGLU, down, combine)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(args, name, wl):
+    """Time one workload's sweep: `warmup` untimed steps, then exactly `steps` timed steps
+    (one launch per M of the sweep each), bracketed by device synchronisations; then each
+    M alone over `steps` back-to-back launches for the per-launch durations."""
     import torch
     import quantized_gemm_amd as qg
     from quantized_gemm_amd import layers, synth
 
-    wl = dict(WORKLOADS[args.workload])
-    if args.sweep:
-        wl["sweep"] = [int(v) for v in args.sweep.split(",")]
-    if args.layer:
-        if args.workload not in LAYERS:
-            print(f"--layer needs an MoE workload ({', '.join(LAYERS)})", file=sys.stderr)
-            sys.exit(2)
-        bench_moe_layer(args, wl)
-        return
-    builder = getattr(synth, args.workload)
+    builder = getattr(synth, name)
     torch.cuda.set_device(0)
     mmax = max(wl["sweep"])
     moe = wl.get("moe")
@@ -473,7 +520,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(wbytes_of[dom] / dom_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.workload, dom) if mfma_bound else None
+    roof["traffic"] = measured_traffic(name, dom) if mfma_bound else None
     roof["kernel"] = f"{'qg_moe_gemm T' if moe else 'qg_gemm M'}={dom}"
 
     result = {
@@ -489,8 +536,68 @@ def main():
         "per_m": per_m,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not moe:
+    return result, builder, layer
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_w4a16_asym_bf16", choices=list(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-cols", type=int, default=8192)
+    ap.add_argument("--sweep", type=str, default="", help="comma-separated M values overriding the workload's sweep")
+    ap.add_argument("--layer", action="store_true",
+                    help="MoE workloads: time the whole layer (align, gate/up, SwiGLU, down, combine)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (no other workloads, no measured ceilings)")
+    ap.add_argument("--ceilings", action="store_true", help="only measure the read and MFMA ceilings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.ceilings:
+        torch.cuda.set_device(0)
+        print(json.dumps({"ceilings": measure_ceilings(args)}), flush=True)
+        return
+    wl = dict(WORKLOADS[args.workload])
+    if args.sweep:
+        wl["sweep"] = [int(v) for v in args.sweep.split(",")]
+    if args.layer:
+        if args.workload not in LAYERS:
+            print(f"--layer needs an MoE workload ({', '.join(LAYERS)})", file=sys.stderr)
+            sys.exit(2)
+        bench_moe_layer(args, wl)
+        return
+    result, builder, layer = run_workload(args, args.workload, wl)
+    if not args.no_cpu_baseline and not wl.get("moe"):
         result["cpu_baseline"] = cpu_baseline(builder, wl, min(args.cpu_cols, layer.n))
+    if not args.no_extras and args.workload == DEFAULT_WORKLOAD and not args.sweep:
+        extras = {}
+        for other in EXTRA_WORKLOADS:
+            r, _, _ = run_workload(args, other, dict(WORKLOADS[other]))
+            extras[other] = {key: r[key] for key in ("value", "unit", "ms_per_step", "dtype", "per_m", "roofline")}
+            extras[other]["workload"] = r["config"]["workload"]
+            torch.cuda.empty_cache()
+        result["other_workloads"] = extras
+        result["ceilings"] = measure_ceilings(args)
+        roof = result["roofline"]
+        ceil = result["ceilings"]["mfma_tflops"].get(wl["dtype"]) if roof["bound"] == "mfma" else \
+            result["ceilings"]["read_GBps"]
+        if ceil:
+            roof["measured_ceiling"] = ceil
+            roof["frac_of_measured"] = round(roof["achieved"] / ceil, 4)
     print(json.dumps(result), flush=True)
 
 

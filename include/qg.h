@@ -135,9 +135,14 @@ typedef struct {
 size_t qg_prepared_bytes(const qg_layer_desc* desc);
 
 /*
- * qg_prepare: the offline transform ("transform()" in the pages: validate, then
- * repack weights, scales and zeros into the layout the kernels read).  One
- * prepared image serves every M and every tile choice.
+ * qg_prepare: the offline transform of a layer.  "Humming: Fast, Flexible Kernels for
+ * Quantized Inference", standard-format paragraph: weights, scales and zero points stay
+ * separate parameters, and a preprocessing step checks them, pads and reorders them into
+ * the layout the kernel reads.  "Humming" (wiki article), "Quantization representation":
+ * the transform runs before the first forward call and its result belongs to one GPU
+ * architecture (here: gfx_arch, checked by every later call).  "Humming" (wiki article),
+ * "Kernel configuration and compilation": one stored layout serves every compute and
+ * tuning choice made per call, so one prepared image serves every M and every tile.
  *   w      device, logical weights of all experts, contiguous:
  *            int4/uint4  uint32 [E][N][K/8]  (element k at bits 4*(k%8), low nibble first)
  *            e2m1        uint8  [E][N][K/2]  (even k in the low nibble)
@@ -156,6 +161,11 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
 /*
  * qg_workspace_bytes: device workspace qg_gemm / qg_moe_gemm need for m rows
  * (dense) or T tokens x topk (MoE; pass topk = 0 for dense).  0 means none.
+ * "Humming" (wiki article), "Device and workload selection": the configuration,
+ * including a split of the reduction, is chosen per range of M; "Precision and
+ * deployment considerations": a Stream-K-style split is a tuning control.  The
+ * workspace holds what such a split (or the W4A8 route below, this library's own
+ * reading) needs between launches.
  *   - dense shapes whose output tiles fill at most half the GPU split K over
  *     workgroups: ksplit * m * N * 4 bytes of fp32 partial sums (required:
  *     QG_ERR_WORKSPACE without it);
@@ -168,6 +178,10 @@ size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t top
 
 /*
  * qg_gemm: dense Y[m, n] = sum_k X[m, k] * W[n, k] for a prepared dense layer.
+ * "Humming" (README), "Usage Example": the quantized layer applied to inputs gives the
+ * product of the inputs with the transposed (dequantized) weight.  "Humming" (wiki
+ * article), "Device and workload selection": the kernel configuration follows the range
+ * of M, switching where compute starts to outweigh the weight traffic.
  *   x        device [M][K] of a_type (f16/bf16 values or e4m3 codes), or packed e2m1 codes
  *            uint8 [M][K/2] for FP4 activations
  *   x_scale  device, else NULL: float32 per-token scales for e4m3 activations, [M], or
@@ -193,7 +207,10 @@ qg_status qg_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int
                           int64_t* cap_sorted, int64_t* cap_blocks);
 
 /*
- * qg_moe_align: token-to-expert sort and padding.
+ * qg_moe_align: token-to-expert sort and padding for the indexed MoE organization
+ * ("Humming" wiki article, "Device and workload selection").  The pages give no
+ * algorithm for it; the contract below (stable order, sentinel, padding) is this
+ * library's.
  *   topk_ids   device int32 [T][topk]; flat index f = t*topk + j; ids outside [0, E) are dropped
  *   sorted_ids device int32 [cap_sorted]: for each expert e in ascending order, the flat
  *              indices routed to e in ascending order, padded with the sentinel T*topk to a
@@ -240,6 +257,9 @@ qg_status qg_moe_grouped_map(int32_t layout, const int32_t* offsets_or_counts, i
 /*
  * qg_moe_gemm: grouped GEMM over the aligned rows.  For every (token t, slot j)
  * with e = topk_ids[t][j] in [0, E):  Y[t*topk + j, :] = X[t] . W_e^T.
+ * "Humming" (wiki article), "Quantization representation": MoE weights carry an expert
+ * dimension; "Device and workload selection": in the indexed organization the kernel
+ * reads each expert's input rows through the routing indices (here sorted_ids).
  *   x        device [T][K] of a_type (FP4: uint8 [T][K/2]);  x_scale device float32 [T] for
  *            e4m3 ([T][K/128] for block-scaled layers), uint8 [T][K/32] for FP4, else NULL
  *   sorted_ids / expert_ids / num_post_pad  from qg_moe_align with the same block_m
@@ -341,6 +361,28 @@ qg_status qg_moe_combine(const void* y, const float* weights, const int32_t* top
  * For checking the prepared layout; not on the GEMM path.
  */
 qg_status qg_dequant(const qg_prepared* p, int32_t expert, float* out, void* stream);
+
+/*
+ * Measurement helpers (not on the GEMM path): the ceilings a kernel's time is read against.
+ * The pages time kernels with a cold L2 ("Humming: Fast, Flexible Kernels for Quantized
+ * Inference", benchmark paragraph) and quote rooflines of bandwidth and matrix throughput
+ * ("Humming" wiki article, "Device and workload selection"); these measure what this GPU
+ * delivers of each.
+ *
+ * qg_ceiling_read: reads `bytes` of buf once with 16-byte loads, loads_per_lane (1, 2, 4,
+ *   8 or 16) per lane, all issued before any is used, in ceil(bytes / (4096 *
+ *   loads_per_lane)) workgroups of 256 lanes; writes one word per wave to sink
+ *   (device uint32, sink_words >= 4 * workgroups, else QG_ERR_WORKSPACE).
+ *   buf device, 16-byte aligned, 0 < bytes < 2^31, bytes % 16 == 0.
+ * qg_ceiling_mfma: `workgroups` workgroups of 4 waves, each wave issuing iters x 4
+ *   independent MFMAs from registers: dtype 0 = bf16 32x32x16 (32768 flop each), 1 = e4m3
+ *   32x32x64 (131072), 2 = e2m1 x e2m1 32x32x64 (131072); sink device float32
+ *   [workgroups * 256].
+ */
+qg_status qg_ceiling_read(const void* buf, uint64_t bytes, int32_t loads_per_lane, uint32_t* sink,
+                          uint64_t sink_words, void* stream);
+qg_status qg_ceiling_mfma(int32_t dtype, int64_t iters, int32_t workgroups, float* sink, uint64_t sink_floats,
+                          void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* qg_status_str(qg_status s);

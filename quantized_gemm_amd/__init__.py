@@ -5,7 +5,8 @@ stream supplies the hipStream_t, and every step of the computation runs in the
 library's HIP kernels.  The entry points mirror include/qg.h one to one:
 ``prepared_bytes``, ``prepare``, ``workspace_bytes``, ``gemm``, ``moe_block_m``,
 ``moe_capacity``, ``moe_align``, ``moe_grouped_map``, ``moe_gemm``, ``moe_swiglu``,
-``moe_combine``, ``quantize_e4m3_rows``, ``dequant``, ``status_str``.
+``moe_combine``, ``quantize_e4m3_rows``, ``quantize_e2m1_rows``, ``dequant``, ``status_str``,
+``version`` and the measurement helpers ``ceiling_read`` and ``ceiling_mfma``.
 
 There is no fallback: if libqg.so is missing or cannot be loaded, every call raises.
 """
@@ -29,7 +30,8 @@ STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_E
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
            "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine",
-           "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_status_str", "qg_version"]
+           "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_ceiling_read", "qg_ceiling_mfma",
+           "qg_status_str", "qg_version"]
 
 
 class QGError(RuntimeError):
@@ -85,6 +87,9 @@ def lib():
         L.qg_quantize_e2m1_rows.argtypes, L.qg_quantize_e2m1_rows.restype = [vp, i64, i64, i32, vp, vp, vp], i32
         L.qg_quantize_e4m3_rows.restype = i32
         L.qg_dequant.argtypes, L.qg_dequant.restype = [pp, i32, vp, vp], i32
+        u64 = ctypes.c_uint64
+        L.qg_ceiling_read.argtypes, L.qg_ceiling_read.restype = [vp, u64, i32, vp, u64, vp], i32
+        L.qg_ceiling_mfma.argtypes, L.qg_ceiling_mfma.restype = [i32, i64, i32, vp, u64, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
         L.qg_version.argtypes, L.qg_version.restype = [], i32
         _lib = L
@@ -213,3 +218,15 @@ def quantize_e2m1_rows(x, rows: int, k: int, in_type: int, codes, scales, stream
 
 def dequant(p: Prepared, expert: int, out, stream=None):
     _check(lib().qg_dequant(ctypes.byref(p), expert, _ptr(out), _stream(stream)), "qg_dequant")
+
+
+def ceiling_read(buf, nbytes: int, loads_per_lane: int, sink, stream=None):
+    """Measurement helper: one streaming read of ``nbytes`` of ``buf`` (see qg_ceiling_read)."""
+    _check(lib().qg_ceiling_read(_ptr(buf), nbytes, loads_per_lane, _ptr(sink), sink.numel(), _stream(stream)),
+           "qg_ceiling_read")
+
+
+def ceiling_mfma(dtype: int, iters: int, workgroups: int, sink, stream=None):
+    """Measurement helper: back-to-back MFMAs (dtype 0 bf16, 1 e4m3, 2 e2m1; see qg_ceiling_mfma)."""
+    _check(lib().qg_ceiling_mfma(dtype, iters, workgroups, _ptr(sink), sink.numel(), _stream(stream)),
+           "qg_ceiling_mfma")

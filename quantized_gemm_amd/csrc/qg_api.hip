@@ -273,8 +273,12 @@ PathInfo widened_path(const PathInfo& pi) {
 // Each workgroup then stages only its slice of K for its rows (one LDS round at 16 rows)
 // instead of all of K; the fp32 partials are summed by the split-K reduction.  1..4 rows
 // keep the 2 x 4 shape without a split (their 4-row staging is already one round).
+// Layers of at most 2^22 weights (2 MiB of 4-bit codes) are launch-bound: they also keep
+// the 2 x 4 shape, K parts added inside the workgroup, so the product is one launch
+// instead of a split plus the reduction's launch.
+constexpr int64_t kTinyWeights = (int64_t)1 << 22;
 int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
-  if (rows <= 4) return 1;
+  if (rows <= 4 || n * k <= kTinyWeights) return 1;
   const int64_t groups = (n / 16 + 7) / 8;
   const int64_t chunks = k / 128;
   int sp = 1;

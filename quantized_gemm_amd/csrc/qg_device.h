@@ -1,9 +1,9 @@
 // Device-side building blocks for the gfx950 quantized GEMM kernels: vector types,
 // MFMA wrappers, bit-unpack / dequant routines for the prepared layout, loads.
 //
-// Prepared layout (format version 1; the transform is "preprocessing ... repacks
-// these tensors into layouts suited to the target kernel" in "Humming: Fast, Flexible
-// Kernels for Quantized Inference"):
+// Prepared layout (format version 1; the offline transform of "Humming: Fast, Flexible
+// Kernels for Quantized Inference", standard-format paragraph, which reorders weights,
+// scales and zero points into the order the kernel reads them):
 //   W: 16-byte units [e][n/16][k/KU][n%16], KU = 32 (4-bit) or 16 (e4m3).  A 4-bit unit is
 //      four u32 words; word j holds k = 8j..8j+7 of the unit, nibble position p holding
 //      element ORDER[p]:  PAIR {0,2,4,6,1,3,5,7} (int4/uint4 with f16/bf16 activations;

@@ -1,6 +1,6 @@
 // Token-to-expert sort and padding for the indexed MoE path ("Humming" wiki article,
-// "Device and workload selection": an indexed path gathers input rows through routing
-// indices).  Counting sort, deterministic and stable, in one launch of G workgroups with
+// "Device and workload selection": the indexed organization reads each expert's input
+// rows through the routing indices).  Counting sort, deterministic and stable, in one launch of G workgroups with
 // no scratch memory: workgroup g owns the contiguous flat-index range [r0, r1).
 //   1. every workgroup counts the expert ids of the whole list (a few hundred KB at most,
 //      read from L2): ids before its range, after it, and inside it per wave (each of its

@@ -1,9 +1,10 @@
 // e4m3 activations -> bf16, exactly (every e4m3 value is a bf16 value), for W4A8 layers
 // run on the 16-bit MFMA path: the int4 weights decode exactly to bf16 there too, and the
 // per-token activation scale is applied in that kernel's epilogue, so the product is the
-// same as multiplying e4m3 by int4 converted to e4m3 ("Humming" wiki article,
-// *Quantization representation*: activations are quantized on the fly; the format of the
-// inner product is the kernel's choice).  Each thread widens 16 codes (16 bytes in, 32 out).
+// same as multiplying e4m3 by int4 converted to e4m3.  Running the W4A8 product in bf16
+// is this library's own reading: the pages fix the operand types (int4 weights converted
+// to FP8 inside the kernel), not the MFMA that multiplies them, and both routes compute the
+// same exact products.  Each thread widens 16 codes (16 bytes in, 32 out).
 #include "qg_device.h"
 #include "qg_kernels.h"
 

@@ -1,15 +1,22 @@
-"""GPU parity at the workloads' full sizes, on sampled outputs.
+"""GPU parity at the workloads' full sizes, over whole output tensors.
 
 Every launch here is the one the benchmark times: the same shapes, the same C-ABI calls
 (qg_gemm with the workspace qg_workspace_bytes asks for; qg_moe_align + qg_moe_gemm with
-the block size qg_moe_block_m picks), hence the same tile, split-K and kernel choice.
-The full outputs are too large for the float64 oracle, so each launch is checked on a
-seeded sample: output rows (dense) or (token, slot) pairs (MoE), always including the
-first and last, times a seeded set of columns including the first and last.  The
-oracle computes those elements one by one from the storage-form weights; the bar is the
-same as for the small cases, max|Y - Y_ref| / max|Y_ref| over the sample, and every
-output element must be finite.
+the block size qg_moe_block_m picks), hence the same tile, split-K and kernel choice; MoE
+sweeps take the first T tokens of one draw at the largest T, as the benchmark does.  The
+whole output is compared element by element with the float64 oracle: dense outputs against
+X . dequant(W)^T, MoE outputs expert by expert (each expert dequantized once and multiplied
+with every (token, slot) row routed to it, over a thread pool).  The bar is the one of the
+small cases, max|Y - Y_ref| / max|Y_ref| over the whole tensor, with any non-finite output
+element a failure (outputs start as NaN, so an unwritten element fails too).
+
+The W4A8 MoE sweep runs twice per T: with the workspace qg_workspace_bytes asks for and with
+none, so both routes the library has for it are checked at full size.  The MoE layers at the
+end of the file check sampled tokens (their oracle needs every gate/up row of a token).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -24,6 +31,7 @@ TOL16 = 5e-3
 TOL8 = 2e-2
 N_ROWS = 24
 N_COLS = 48
+POOL = max(1, min(8, (os.cpu_count() or 4) // 2))
 
 
 def _tol(layer):
@@ -35,86 +43,150 @@ def _sample(rng, total, count):
     return np.unique(np.concatenate([pick, [0, total - 1]]))
 
 
-def _dense_check(layer, acts, m, seed):
-    p, buf = layers.prepare_layer(layer)
-    x, xs = layers.acts_to_dev(acts)
-    x, xs = x[:m], (None if xs is None else xs[:m])
-    y = torch.full((m, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
-    ws = torch.zeros(max(1, qg.workspace_bytes(p, m)), dtype=torch.uint8, device="cuda")
-    qg.gemm(p, x, xs, y, m, ws)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all()), "non-finite output"
-    rng = np.random.default_rng(seed)
-    rows, cols = _sample(rng, m, N_ROWS), _sample(rng, layer.n, N_COLS)
-    got = layers.out_bits_to_f64(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
-    sub = synth.Acts(acts.x[rows], None if acts.x_scale is None else acts.x_scale[rows], None)
-    ref = R.dense_gemm(R.activations(sub, layer.a_type), R.dequant_rows(layer, 0, cols))
-    err = R.relative_error(got, ref)
-    assert err <= _tol(layer), f"m={m}: relative error {err:.3g}"
+# ---- dense ----------------------------------------------------------------------------------
+
+class _Dense:
+    """One full-size dense layer on the GPU and its float64 dequantized weights."""
+
+    def __init__(self, layer, acts):
+        self.layer, self.acts = layer, acts
+        self.p, self.buf = layers.prepare_layer(layer)
+        self.x, self.xs = layers.acts_to_dev(acts)
+        self.w_ref = R.dequant_layer(layer, 0)
+        self.x_ref = R.activations(acts, layer.a_type)
+
+    def check(self, m):
+        lay = self.layer
+        y = torch.full((m, lay.n), float("nan"), dtype=layers.out_dtype(lay), device="cuda")
+        ws = torch.zeros(max(1, qg.workspace_bytes(self.p, m)), dtype=torch.uint8, device="cuda")
+        qg.gemm(self.p, self.x[:m], None if self.xs is None else self.xs[:m], y, m, ws)
+        torch.cuda.synchronize()
+        got = layers.out_bits_to_f64(y)
+        ref = R.dense_gemm(self.x_ref[:m], self.w_ref)
+        err = R.relative_error(got, ref)
+        assert err <= _tol(lay), f"m={m}: relative error {err:.3g} over the whole {m} x {lay.n} output"
 
 
 @pytest.fixture(scope="module")
 def c2():
-    return synth.dense_w4a16_asym_bf16(m=4096, n=8192, k=8192, seed=0)
+    d = _Dense(*synth.dense_w4a16_asym_bf16(m=4096, n=8192, k=8192, seed=0))
+    yield d
+    del d
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("m", [1, 16, 128, 1024, 4096])
 def test_dense_w4a16_asym_bf16_8192(c2, m):
-    layer, acts = c2
-    _dense_check(layer, acts, m, seed=m)
+    c2.check(m)
 
 
 @pytest.fixture(scope="module")
 def c3():
-    return synth.dense_w8a8_fp8(m=4096, n=7168, k=7168, seed=0)
+    d = _Dense(*synth.dense_w8a8_fp8(m=4096, n=7168, k=7168, seed=0))
+    yield d
+    del d
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("m", [1, 64, 512, 4096])
 def test_dense_w8a8_fp8_7168(c3, m):
-    layer, acts = c3
-    _dense_check(layer, acts, m, seed=m)
+    c3.check(m)
 
 
-def _moe_check(layer, acts, seed):
-    t, topk = acts.topk_ids.shape
-    p, buf = layers.prepare_layer(layer)
+def test_dense_w4a16_sym_f16_512x1024():
+    d = _Dense(*synth.dense_w4a16_sym_f16(m=16, n=512, k=1024, seed=0))
+    d.check(16)
+
+
+# ---- MoE ------------------------------------------------------------------------------------
+
+def _moe_gpu(p, layer, acts, t, with_ws=True):
+    """One MoE launch on the first t tokens, as the benchmark makes it; output [t * topk, N] float64."""
+    topk = acts.topk_ids.shape[1]
     bm = qg.moe_block_m(p, t, topk)
     cs, cb = qg.moe_capacity(t, topk, layer.experts, bm)
-    ids = torch.from_numpy(np.ascontiguousarray(acts.topk_ids, dtype=np.int32)).cuda()
+    ids = torch.from_numpy(np.ascontiguousarray(acts.topk_ids[:t], dtype=np.int32)).cuda()
     sid = torch.empty(cs, dtype=torch.int32, device="cuda")
     eid = torch.empty(cb, dtype=torch.int32, device="cuda")
     npp = torch.empty(1, dtype=torch.int32, device="cuda")
     qg.moe_align(ids, t, topk, layer.experts, bm, sid, eid, npp)
     x, xs = layers.acts_to_dev(acts)
+    x, xs = x[:t], (None if xs is None else xs[:t])
     y = torch.full((t * topk, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
-    ws = torch.zeros(max(1, qg.workspace_bytes(p, t, topk)), dtype=torch.uint8, device="cuda")
+    nws = qg.workspace_bytes(p, t, topk) if with_ws else 0
+    ws = torch.zeros(max(1, nws), dtype=torch.uint8, device="cuda") if nws else None
     qg.moe_gemm(p, x, xs, sid, eid, npp, t, topk, bm, y, ws)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all()), "non-finite output"
-    rng = np.random.default_rng(seed)
-    slots, cols = _sample(rng, t * topk, N_ROWS), _sample(rng, layer.n, N_COLS)
-    got = layers.out_bits_to_f64(y[torch.from_numpy(slots).cuda()][:, torch.from_numpy(cols).cuda()])
-    tok = slots // topk
-    xa = R.activations(synth.Acts(acts.x[tok], None if acts.x_scale is None else acts.x_scale[tok], None),
-                       layer.a_type)
-    ref = np.empty_like(got)
-    for i, sl in enumerate(slots):
-        e = int(acts.topk_ids[sl // topk, sl % topk])
-        ref[i] = R.dense_gemm(xa[i:i + 1], R.dequant_rows(layer, e, cols))[0]
-    err = R.relative_error(got, ref)
-    assert err <= _tol(layer), f"T={t}: relative error {err:.3g}"
+    return layers.out_bits_to_f64(y)
 
 
-@pytest.mark.parametrize("t", [16, 256, 4096])
-def test_moe_w4a16_mxfp4_e128(t):
-    layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=128, topk=8, n=4096, k=7168, seed=0)
-    _moe_check(layer, acts, seed=t)
+def _moe_reference(layer, acts, ts):
+    """Oracle outputs [t * topk, N] for every t in ts (first t tokens), one expert at a time."""
+    ids = np.asarray(acts.topk_ids)
+    topk = ids.shape[1]
+    x = R.activations(acts, layer.a_type)
+    refs = {t: np.full((t * topk, layer.n), np.nan) for t in ts}
+    tmax = max(ts)
+    used = np.unique(ids[:tmax][(ids[:tmax] >= 0) & (ids[:tmax] < layer.experts)])
+
+    def one(e):
+        tt, jj = np.nonzero(ids[:tmax] == e)
+        y = R.dense_gemm(x[tt], R.dequant_layer(layer, int(e)))
+        for t in ts:                     # rows are disjoint across experts: no write conflicts
+            sel = tt < t
+            refs[t][tt[sel] * topk + jj[sel]] = y[sel]
+
+    with ThreadPoolExecutor(POOL) as ex:
+        list(ex.map(one, used))
+    return refs
 
 
-@pytest.mark.parametrize("t", [64, 1024, 8192])
-def test_moe_w4a8_int4_e64_skewed(t):
-    layer, acts = synth.moe_w4a8_int4(t=t, experts=64, topk=6, n=2816, k=4096, seed=0)
-    _moe_check(layer, acts, seed=t)
+class _MoE:
+    def __init__(self, layer, acts, ts, routes=(True,)):
+        self.layer = layer
+        p, buf = layers.prepare_layer(layer)
+        self.got = {(t, r): _moe_gpu(p, layer, acts, t, with_ws=r) for t in ts for r in routes}
+        del buf
+        torch.cuda.empty_cache()
+        self.ref = _moe_reference(layer, acts, ts)
+
+    def check(self, t, route=True):
+        g, r = self.got[(t, route)], self.ref[t]
+        assert not np.isnan(r).any(), "every (token, slot) row is routed to a valid expert here"
+        err = R.relative_error(g, r)
+        assert err <= _tol(self.layer), f"T={t}: relative error {err:.3g} over the whole {g.shape} output"
+
+
+C4_T = [16, 256, 4096]
+C5_T = [64, 1024, 8192]
+
+
+@pytest.fixture(scope="module")
+def c4():
+    d = _MoE(*synth.moe_w4a16_mxfp4(t=max(C4_T), experts=128, topk=8, n=4096, k=7168, seed=0), C4_T)
+    yield d
+    del d
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("t", C4_T)
+def test_moe_w4a16_mxfp4_e128(c4, t):
+    c4.check(t)
+
+
+@pytest.fixture(scope="module")
+def c5():
+    d = _MoE(*synth.moe_w4a8_int4(t=max(C5_T), experts=64, topk=6, n=2816, k=4096, seed=0), C5_T,
+             routes=(True, False))
+    yield d
+    del d
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("route", [True, False], ids=["workspace", "no_workspace"])
+@pytest.mark.parametrize("t", C5_T)
+def test_moe_w4a8_int4_e64_skewed(c5, t, route):
+    c5.check(t, route)
 
 
 # ---- whole MoE layers at full size ----------------------------------------------------------
