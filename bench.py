@@ -35,8 +35,8 @@ MFMA_SOURCES = ["qg_mfma_kernel.h", "qg_device.h", "qg_kernels.h", "qg_mfma_int4
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 
 # Workloads: (builder, sweep, arithmetic type of the MFMAs (selects the peak), description).
-# The W4A8 layer runs with the workspace qg_workspace_bytes asks for, so its products are
-# bf16 MFMAs at every size (the int4 codes and e4m3 activations both widen exactly).
+# The W4A8 products run on fp8 MFMAs (int4 converted to e4m3 in the kernel) above the
+# streaming sizes; below them the streaming kernel multiplies exact bf16 images of both.
 WORKLOADS = {
     "dense_w4a16_asym_bf16": dict(sweep=[1, 16, 128, 1024, 4096], n=8192, k=8192, dtype="bf16",
                                   desc="dense W4A16 uint4 + uint4 zero points, bf16 group-128 scales, "
@@ -63,7 +63,7 @@ WORKLOADS = {
     "moe_w4a4_mxfp4": dict(sweep=[16, 256, 4096], n=4096, k=7168, dtype="fp4", moe=dict(experts=128, topk=8),
                            desc="MoE W4A4 MXFP4 (e2m1 + UE8M0/32 on both sides, scaled fp4 x fp4 MFMAs), E=128 "
                                 "top-8, fused gate+up N=4096, K=7168; T sweep"),
-    "moe_w4a8_int4": dict(sweep=[64, 1024, 8192], n=2816, k=4096, dtype="bf16", moe=dict(experts=64, topk=6),
+    "moe_w4a8_int4": dict(sweep=[64, 1024, 8192], n=2816, k=4096, dtype="fp8", moe=dict(experts=64, topk=6),
                           desc="MoE W4A8 int4 weights with bf16 group-128 scales x per-token e4m3 activations, "
                                "E=64 top-6, N=2816, K=4096, 20% of tokens biased to 4 hot experts; T sweep"),
 }

@@ -29,9 +29,9 @@
  * - M == 0 (or T == 0) is a successful no-op.
  * - Row-major tensors with contiguous rows; every pointer must be 16-byte aligned.
  * - Workspaces: when qg_workspace_bytes() is non-zero the caller passes a device
- *   buffer of at least that size whose bytes are ZERO before its first use (e.g.
- *   allocated with a zero fill).  Every call leaves it ready for the next call; calls
- *   that share one workspace must not run concurrently (use one per stream).
+ *   buffer of at least that size; its contents need no initialisation (a call writes
+ *   every byte it reads).  Calls that share one workspace must not run concurrently
+ *   (use one per stream).
  * - Shape rules: n % 64 == 0, k % 128 == 0, k % group_k == 0.
  */
 #ifndef QG_H_
@@ -75,8 +75,7 @@ enum { QG_C_NATIVE = 0,    /* multiply in the activation's type                 
         * "Precision and deployment considerations": no Stream-K-style split and the same
         * MMA type across batch sizes).  Every row count then runs the MFMA kernel without a
         * split over K, so each output row is bitwise the same whatever M (or T) and the other
-        * rows are; slower at small M.  MoE block sizes below 128 are rejected.  W4A8 layers
-        * must be given (or denied) the widening workspace consistently across calls. */
+        * rows are; slower at small M.  MoE block sizes below 128 are rejected. */
        QG_C_BATCH_INVARIANT = 4 };
 
 /*
@@ -169,10 +168,7 @@ qg_status qg_prepare(const qg_layer_desc* desc, const void* w, const void* scale
  *   - dense shapes whose output tiles fill at most half the GPU split K over
  *     workgroups: ksplit * m * N * 4 bytes of fp32 partial sums (required:
  *     QG_ERR_WORKSPACE without it);
- *   - W4A8 layers (int4 -> e4m3 compute) above the weight-streaming sizes: the
- *     activations widened to bf16, rows * K * 2 bytes.  Optional: with it the
- *     product runs on the 16-bit MFMA path (exact widening, per-token scale in the
- *     epilogue), without it on the e4m3 MFMA path.
+ *   - grouped (MoE) products need none.
  */
 size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t topk);
 

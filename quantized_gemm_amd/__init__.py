@@ -230,3 +230,4 @@ def ceiling_mfma(dtype: int, iters: int, workgroups: int, sink, stream=None):
     """Measurement helper: back-to-back MFMAs (dtype 0 bf16, 1 e4m3, 2 e2m1; see qg_ceiling_mfma)."""
     _check(lib().qg_ceiling_mfma(dtype, iters, workgroups, _ptr(sink), sink.numel(), _stream(stream)),
            "qg_ceiling_mfma")
+

@@ -207,17 +207,16 @@ StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
 constexpr int kCUs = 256;
 constexpr int64_t kStreamMaxRows = 64;
 
-// The int4 -> e4m3 kernel uses 128-row tiles only.
-bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_INT4Q_FP8 && pi.wp_mfma != WP_FP8_BLOCK; }
+// The block-scaled e4m3 kernel uses 128-row tiles only.
+bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8_BLOCK; }
 
 // Split K over workgroups when 128-row tiles would fill at most half of the CUs (above
 // that, writing and re-reading the fp32 partials costs more than the idle CUs):
 // the largest power of two (at most 8) that keeps the grid within one workgroup per
-// CU, leaves every slice whole scale groups and at least 8 K steps.  Not for the
-// int4 -> e4m3 kernel.
+// CU, leaves every slice whole scale groups and at least 8 K steps.
 constexpr int kMaxSplit = 8;
 int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
-  if (pi.wp_mfma == WP_INT4Q_FP8 || pi.binv || tiles * 2 > kCUs) return 1;
+  if (pi.binv || tiles * 2 > kCUs) return 1;
   const int64_t bk = pi.af == A_FP8 ? 128 : 64;   // K per step: fp8 MFMAs take 128
   const int64_t steps = k / bk;
   int sp = 1;
@@ -241,31 +240,13 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   t.ksplit = t.bm == 128 ? split_for(tiles, k, group, pi) : 1;
   // experiment-only override of the split (QG_KSPLIT=1|2|4|8; slices must stay whole groups)
   static const char* ks = getenv("QG_KSPLIT");
-  if (ks && t.bm == 128 && pi.wp_mfma != WP_INT4Q_FP8 && !pi.binv) {
+  if (ks && t.bm == 128 && !pi.binv) {
     const int v = atoi(ks);
     const int64_t bk = pi.af == A_FP8 ? 128 : 64;
     if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / bk) % v == 0 && (group <= 0 || (k / v) % group == 0))
       t.ksplit = v;
   }
   return t;
-}
-
-// W4A8 above the streaming sizes: with a workspace for the activations widened to bf16,
-// the 16-bit MFMA kernel runs the product (QUAD int4 decoded exactly to bf16, per-token
-// scale in its epilogue); without one, the e4m3 MFMA kernel with per-group promotion.
-bool is_w4a8(const PathInfo& pi) { return pi.wp_small == WP_INT4Q_MAGIC; }
-size_t widened_bytes(const qg_prepared* p, int64_t rows) {
-  return ((size_t)rows * (size_t)p->desc.k * 2 + 255) / 256 * 256;
-}
-bool widen_ok(const qg_prepared* p, int64_t rows, const void* ws, size_t ws_bytes) {
-  const size_t need = widened_bytes(p, rows);
-  return ws && aligned16(ws) && ws_bytes >= need && need < ((size_t)1 << 31);   // one buffer resource
-}
-PathInfo widened_path(const PathInfo& pi) {
-  PathInfo w = pi;
-  w.wp_mfma = WP_INT4Q_MAGIC;
-  w.af = A_BF16;
-  return w;
 }
 
 // Dense weight streaming for 5..64 rows: workgroups of 8 column blocks (128 columns) x 1 K
@@ -279,6 +260,12 @@ PathInfo widened_path(const PathInfo& pi) {
 constexpr int64_t kTinyWeights = (int64_t)1 << 22;
 int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
   if (rows <= 4 || n * k <= kTinyWeights) return 1;
+  // experiment-only override (QG_STREAM_SPLIT=1|2|4|8; slices must stay whole groups)
+  static const char* ov = getenv("QG_STREAM_SPLIT");
+  if (ov) {
+    const int v = atoi(ov);
+    if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / 128) % v == 0 && (group <= 0 || (k / v) % group == 0)) return v;
+  }
   const int64_t groups = (n / 16 + 7) / 8;
   const int64_t chunks = k / 128;
   int sp = 1;
@@ -306,7 +293,7 @@ MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
   return t;
 }
 
-// Workspace of a dense call: the split-K partial sums, or W4A8's widened activations.
+// Workspace of a dense call: the split-K partial sums.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
   if (pi.af == A_FP4) return 0;   // W4A4 splits K only inside a workgroup
   if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
@@ -317,7 +304,6 @@ size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
     const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
     return sp > 1 ? (size_t)sp * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
   }
-  if (is_w4a8(pi)) return widened_bytes(p, m);
   const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
   return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
 }
@@ -387,9 +373,7 @@ size_t qg_workspace_bytes(const qg_prepared* p, int64_t m_or_tokens, int32_t top
   PathInfo pi;
   if (check_prepared(p, &pi) != QG_OK || m_or_tokens <= 0) return 0;
   if (topk == 0 && p->desc.num_experts == 1) return dense_workspace(p, pi, m_or_tokens);
-  if (topk > 0 && is_w4a8(pi) && qg_moe_block_m(p, m_or_tokens, topk) > kStreamMaxRows)
-    return widened_bytes(p, m_or_tokens);          // the tokens' activations, widened
-  return 0;
+  return 0;                                         // grouped products need none
 }
 
 static void fill_stream_args(StreamArgs& a, const qg_prepared* p) {
@@ -481,22 +465,10 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
     return launched();
   }
   const bool mfma = m > kStreamMaxRows || pi.binv;   // batch-invariant: one MMA type for every M
-  if (mfma && is_w4a8(pi) && widen_ok(p, m, ws, ws_bytes)) {
-    const PathInfo pw = widened_path(pi);
-    MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pw);
-    t.ksplit = 1;
-    launch_widen_e4m3_bf16(x, ws, m * p->desc.k, (hipStream_t)stream);
-    a.x = ws;
-    QG_LOG("gemm m=%lld n=%lld k=%lld -> widened e4m3, mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
-           (long long)p->desc.k, t.bm, t.grid_x);
-    if (!launch_mfma_gemm(a, t, pw.wp_mfma, pw.af, pw.of, pw.st, false, false, (hipStream_t)stream))
-      return QG_ERR_UNSUPPORTED;
-    return launched();
-  }
   if (mfma) {
     const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
     if (t.ksplit > 1) {
-      const size_t need = dense_workspace(p, pi, m);
+      const size_t need = (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float);
       if (!ws || !aligned16(ws) || ws_bytes < need) return QG_ERR_WORKSPACE;
       a.part = (float*)ws;
       a.ksplit = t.ksplit;
@@ -657,16 +629,6 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, 
     t.bm = block_m;
     t.grid_x = (unsigned)((p->desc.n + 255) / 256);
     t.grid_y = (unsigned)cb;
-    if (is_w4a8(pi) && widen_ok(p, tokens, ws, ws_bytes)) {
-      const PathInfo pw = widened_path(pi);
-      launch_widen_e4m3_bf16(x, ws, tokens * p->desc.k, (hipStream_t)stream);
-      a.x = ws;
-      QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> widened e4m3, mfma grid=%ux%u", (long long)tokens, topk, block_m,
-             t.grid_x, t.grid_y);
-      if (!launch_mfma_gemm(a, t, pw.wp_mfma, pw.af, pw.of, pw.st, false, true, (hipStream_t)stream))
-        return QG_ERR_UNSUPPORTED;
-      return launched();
-    }
     QG_LOG("moe_gemm T=%lld topk=%d bm=%d -> mfma grid=%ux%u", (long long)tokens, topk, block_m, t.grid_x, t.grid_y);
     if (!launch_mfma_gemm(a, t, pi.wp_mfma, pi.af, pi.of, pi.st, p->desc.has_zero != 0, true, (hipStream_t)stream))
       return QG_ERR_UNSUPPORTED;

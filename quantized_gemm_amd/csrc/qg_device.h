@@ -91,14 +91,23 @@ __device__ __forceinline__ uint16_t f32_to_out(float v) {
 // Magic-number decode: OR a nibble into the mantissa of 1.0.  bf16: 1 + u/128
 // (0x3F80 | u), f16: 1 + u/1024 (0x3C00 | u); both exact.  Dword q of the result holds
 // the nibbles at positions q (low half) and q+4 (high half) of the word.
+// The compiler selects one v_and_or_b32 for (x & mask) | bits when neither constant is a
+// literal (VOP3 takes no literal operand on this GPU and reads at most one SGPR), so the
+// mask is pinned in a VGPR and the OR-ed bits in an SGPR by empty asm statements; with
+// literals it emits v_and + v_or.  The instruction itself stays compiler-generated, so its
+// hazards against the MFMAs that read the result are tracked (a hand-written v_and_or_b32 in
+// inline asm is invisible to that tracking).
 template <int AF>
 __device__ __forceinline__ u32x4 magic4(uint32_t w) {
   constexpr uint32_t M = (AF == A_F16) ? 0x3C003C00u : 0x3F803F80u;
+  uint32_t mask = 0x000F000Fu, bits = M;
+  asm("" : "+v"(mask));
+  asm("" : "+s"(bits));
   u32x4 r;
-  r[0] = (w & 0x000F000Fu) | M;
-  r[1] = ((w >> 4) & 0x000F000Fu) | M;
-  r[2] = ((w >> 8) & 0x000F000Fu) | M;
-  r[3] = ((w >> 12) & 0x000F000Fu) | M;
+  r[0] = (w & mask) | bits;
+  r[1] = ((w >> 4) & mask) | bits;
+  r[2] = ((w >> 8) & mask) | bits;
+  r[3] = ((w >> 12) & mask) | bits;
   return r;
 }
 template <int AF> struct MagicConst;

@@ -21,7 +21,6 @@ bool mfma_int4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool,
 bool mfma_fp4(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 bool mfma_fp8(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 bool mfma_w4a8(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
-bool mfma_int4q(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 bool mfma_fp8_block(const MfmaArgs&, const MfmaTile&, int, int, int, int, bool, bool, hipStream_t);
 
 bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int of, int stype, bool zero, bool moe,
@@ -30,7 +29,6 @@ bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int 
   if (mfma_fp4(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (mfma_fp8(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (mfma_w4a8(a, t, wp, af, of, stype, zero, moe, st)) return true;
-  if (mfma_int4q(a, t, wp, af, of, stype, zero, moe, st)) return true;
   if (mfma_fp8_block(a, t, wp, af, of, stype, zero, moe, st)) return true;
   return false;
 }

@@ -47,9 +47,6 @@ bool launch_mfma_gemm(const MfmaArgs& a, const MfmaTile& t, int wp, int af, int 
 // (w_scale, fp8 weights) and per-token (a.x_scale, e4m3 activations) scales.
 bool launch_split_reduce(const MfmaArgs& a, bool w_scale, bool x_scale, int of, hipStream_t st);
 
-// e4m3 codes -> bf16 values (exact); elems a multiple of 16, both buffers 16-byte aligned.
-void launch_widen_e4m3_bf16(const void* x, void* y, int64_t elems, hipStream_t st);
-
 bool launch_stream_gemm(const StreamArgs& a, const StreamTile& t, int wp, int af, int of, int stype, bool zero,
                         bool moe, hipStream_t st);
 

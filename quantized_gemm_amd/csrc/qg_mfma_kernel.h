@@ -6,6 +6,9 @@
 // conversion is spread over BM rows:
 //   * int4 / uint4: nibble -> float (v_cvt_f32_ubyteN), (u - z) * s as one exact FMA
 //     with z*s precomputed, rounded once to bf16/f16;
+//   * int4 x e4m3 (W4A8): int4 -> e4m3 by a byte table (exact), fp8 MFMA (32x32x64) per
+//     128-wide step = one scale group, each step's product promoted by its group scale,
+//     per-token scale in the epilogue;
 //   * e2m1: hardware e2m1 -> bf16/f16 conversion with the UE8M0 scale folded in;
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
 //     in the epilogue;
@@ -39,6 +42,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F4A = (AF == A_FP4);                // e2m1 activations: fp4 x fp4 MFMAs
   constexpr bool F8 = (AF == A_FP8) || F4A;          // byte operands to scaled / fp8 MFMAs as stored
   constexpr bool FP4B = (AF == A_FP8) && WP == WP_FP4;   // e4m3 activations with e2m1 weights
+  constexpr bool I4F8 = (AF == A_FP8) && WP == WP_INT4Q_FP8;   // int4 weights converted to e4m3 here
   constexpr int AB = F8 ? 1 : 2;
   constexpr int BK = F4A ? 256 : F8 ? 128 : 64;   // K per step; one LDS row segment = 128 bytes
   constexpr int NTHR = 64 * CW;              // CW waves, each owning BN / CW columns and all BM rows
@@ -50,11 +54,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int STAGE = BM * ROWB;
   constexpr int NS = 3;                      // activation stages in LDS (ring)
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
-  constexpr int BU = F8 ? (FP4B ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step (F4A: 4)
-  // elements held by the bytes of the low / high nibble words of a 4-bit code word
-  constexpr bool QUAD = (WP == WP_INT4Q_MAGIC);
-  constexpr int M0[4] = {0, QUAD ? 1 : 4, QUAD ? 2 : 1, QUAD ? 3 : 5};
-  constexpr int M1[4] = {QUAD ? 4 : 2, QUAD ? 5 : 6, QUAD ? 6 : 3, 7};
+  constexpr int BU = F8 ? ((FP4B || I4F8) ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step (F4A: 4)
+  // elements held by the bytes of the low / high nibble words of a 4-bit code word (PAIR order)
+  constexpr int M0[4] = {0, 4, 1, 5};
+  constexpr int M1[4] = {2, 6, 3, 7};
 
   // one array per stage: the compiler then sees which stage an LDS read and an
   // HBM->LDS load touch, and waits only where they really overlap
@@ -269,10 +272,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
       for (int u = 0; u < BU; ++u) {
         // 4-bit: unit (step*2 + g) covers k = 64*step + 32g ..; fp8: units 8*step + 4g + u;
         // e2m1 under e4m3 activations: unit 4*step + 2u + g covers k = 128*step + 64u + 32g ..,
-        // the e2m1 operand of MFMA u on this lane; under e2m1 activations unit 8*step + 2u + g
+        // the e2m1 operand of MFMA u on this lane (int4 converted to e4m3: the same units, each
+        // becoming the 32-byte operand of MFMA u); under e2m1 activations unit 8*step + 2u + g
         // (k = 256*step + 64u + 32g ..), the operand of MFMA u
         const int64_t gs = (int64_t)(kstep0 + step);
-        const int64_t ku = F4A ? gs * 8 + 2 * u + g : F8 ? (FP4B ? gs * 4 + 2 * u + g : gs * 8 + 4 * g + u) : (gs * 2 + g);
+        const int64_t ku = F4A ? gs * 8 + 2 * u + g
+                         : F8 ? ((FP4B || I4F8) ? gs * 4 + 2 * u + g : gs * 8 + 4 * g + u) : (gs * 2 + g);
         const bool ok = wok[t] && step < nsteps;
         // cached: every weight tile is read again by the other row tiles of the XCD
         dst[t][u] = bload16(wr, ok ? (int)(((nb * kun + ku) * 16 + c) << 4) : kOOB);
@@ -303,7 +308,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
         const int64_t gi = (int64_t)(kstep0 + step) * 2 + g;   // group 32 == unit
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         zs[t] = 0.f;
-      } else if constexpr (WP == WP_INT4_MAGIC || WP == WP_INT4Q_MAGIC) {
+      } else if constexpr (I4F8) {
+        // one step (128 K) lies inside one scale group: the step's products are promoted by it
+        const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
+        s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
+        zs[t] = 0.f;
+      } else if constexpr (WP == WP_INT4_MAGIC) {
         const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         float z = 8.0f;
@@ -376,11 +386,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
         Bq[t] = fp4_to_16<AF>(w, sc[t]);
       } else {
         // PAIR nibble order (biased u = q + 8 or uint4): bytes of x0 hold elements
-        // (0,4,1,5), bytes of x1 (2,6,3,7).  QUAD order (two's complement int4, XOR-ed to
-        // q + 8 here): bytes of x0 hold elements 0..3, of x1 4..7.  The empty asm hides
-        // where x0/x1 come from so that each byte converts with a single
-        // v_cvt_f32_ubyteN instead of a bit-field extract plus a conversion.
-        const uint32_t wb = WP == WP_INT4Q_MAGIC ? (w ^ 0x88888888u) : w;
+        // (0,4,1,5), bytes of x1 (2,6,3,7).  The empty asm hides where x0/x1 come from so
+        // that each byte converts with a single v_cvt_f32_ubyteN instead of a bit-field
+        // extract plus a conversion.
+        const uint32_t wb = w;
         uint32_t x0 = wb & 0x0F0F0F0Fu, x1 = (wb >> 4) & 0x0F0F0F0Fu;
         asm volatile("" : "+v"(x0), "+v"(x1));
         float e[8];
@@ -410,9 +419,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
       out[stg] = (AF == A_F16) ? fp4_to_16<A_F16>(w, sc[t])[stg] : fp4_to_16<A_BF16>(w, sc[t])[stg];
     } else {
       if (stg == 0) {
-        const uint32_t wb = WP == WP_INT4Q_MAGIC ? (w ^ 0x88888888u) : w;
-        d.x0 = wb & 0x0F0F0F0Fu;
-        d.x1 = (wb >> 4) & 0x0F0F0F0Fu;
+        d.x0 = w & 0x0F0F0F0Fu;
+        d.x1 = (w >> 4) & 0x0F0F0F0Fu;
         asm volatile("" : "+v"(d.x0), "+v"(d.x1));   // keep v_cvt_f32_ubyteN (see dequant)
       } else if (stg == 1) {
         d.e[M0[0]] = __builtin_fmaf((float)(d.x0 & 0xFF), sc[t], zs[t]);
@@ -529,6 +537,63 @@ void mfma_gemm_kernel(MfmaArgs a) {
           acc[mt][t] = mfma32x32x64_fp4_fp4(Af4[q % (AH + 1)], B, sa4[q % (AH + 1)],
                                             (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu), acc[mt][t]);
           keep_in_vgprs(acc[mt][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (I4F8) {
+      // int4 -> e4m3 (exact, a byte table per 4 weights): each of the lane's two units
+      // (32 K of its column, QUAD order) becomes the 32-byte e4m3 operand of one 32x32x64
+      // MFMA, in k order; the activation operand is the same 32 K of the row (chunks 4j + 2g
+      // and 4j + 2g + 1 of the row segment), so both sides share one k order.
+      i32x8 Bc[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 e = int4q_to_e4m3(b0[t][u][j]);
+            Bc[t][u][2 * j] = (int)e[0];
+            Bc[t][u][2 * j + 1] = (int)e[1];
+          }
+      auto read_a8i = [&](int mt, int j) -> i32x8 {
+        const int row = 32 * mt + r;
+        const int lc0 = 4 * j + 2 * g;
+        const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
+        const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
+        i32x8 A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
+        return A;
+      };
+      // The step is one scale group: each row tile's product P over the step's 128 K starts
+      // from zero (two MFMAs) and is promoted, acc += s * P, one row tile behind, so that the
+      // promotion of tile mt - 1 runs while the MFMAs of tile mt do; activation fragments
+      // (q = 2 mt + j) are read one MFMA ahead.
+      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      i32x8 Ai[2];
+      f32x16 P[2][NT];
+      Ai[0] = read_a8i(0, 0);
+#pragma unroll
+      for (int mt = 0; mt <= MT; ++mt) {
+        if (mt < MT) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int q = 2 * mt + j;
+            if (q + 1 < 2 * MT) Ai[(q + 1) & 1] = read_a8i((q + 1) >> 1, (q + 1) & 1);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              P[mt & 1][t] = mfma32x32x64_fp8(Ai[q & 1], Bc[t][j], j == 0 ? zero16 : P[mt & 1][t]);
+          }
+        }
+        if (mt > 0) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              acc[mt - 1][t][i] = __builtin_fmaf(scl[S][t], P[(mt - 1) & 1][t][i], acc[mt - 1][t][i]);
+            keep_in_vgprs(acc[mt - 1][t]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -687,7 +752,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
             *(float*)(ep + rl * PITCH + (32 * t + r) * 4) = v;
           } else {
             v *= sw[t];
-            if constexpr (AF == A_FP8 || WP == WP_INT4Q_MAGIC) {   // per-token scale (e4m3 activations)
+            if constexpr (AF == A_FP8) {   // per-token scale (e4m3 activations)
               const int tok = sRowTok[rbase + rl];
               v *= tok < 0 ? 0.f : a.x_scale[tok];
             }
@@ -723,7 +788,7 @@ static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // (their blocks are many and short, and independent workgroups hide each other's barriers
   // better: measured 15% faster for 16-bit, 13-21% for e2m1 x e4m3, while dense 128-row
   // tiles gain ~10% from 8 waves and 4-wave e4m3-weight tiles spill).
-  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8 || AF == A_FP4) ? 8 : 4;
+  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8 || WP == WP_INT4Q_FP8 || AF == A_FP4) ? 8 : 4;
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 

@@ -236,10 +236,10 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
   f32x4 acc[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the lane's activation row within a 16-row tile: staged rows only (4-row tiles: rows
-  // 4..15 read row r & 3 and are then zeroed)
+  // the lane's activation row within a 16-row tile: staged rows only.  4-row tiles: rows
+  // 4..15 of the MFMA operand read row r & 3 again; the products of those rows are finite
+  // copies that land in accumulator rows 4..15, which nothing stores, so they need no zeroing
   const int ar = MT == 0 ? (r & 3) : r;
-  const bool aok = MT != 0 || r < 4;
 
   const int nrounds = (per + RCR - 1) / RCR;
 
@@ -312,12 +312,12 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                 i32x8 A, B;
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  A[i] = aok ? (int)a0[i] : 0; A[4 + i] = aok ? (int)a1[i] : 0;
+                  A[i] = (int)a0[i]; A[4 + i] = (int)a1[i];
                   B[i] = (int)bw[c][0][i]; B[4 + i] = (int)bw[c][1][i];
                 }
                 if constexpr (BLOCK) {
                   // rows 16mt + 4g .. + 3 of the lane's accumulator (4-row tiles: lanes g > 0
-                  // hold the zero rows 4..15)
+                  // hold the copied rows 4..15, scaled by 0 here and never stored)
                   const f32x4 P = mfma16x16x128_fp8(A, B, f32x4{0.f, 0.f, 0.f, 0.f});
                   const int rs = (q * RCR + lc) * BM + 16 * mt + 4 * g;
                   const f32x4 sa4 = (16 * mt + 4 * g + 3 < BM) ? *(const f32x4*)&sSA[rs] : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                 const u32x4 a0 = *(const u32x4*)ap, a1 = *(const u32x4*)(ap + 64);
                 i32x8 A;
     #pragma unroll
-                for (int i = 0; i < 4; ++i) { A[i] = aok ? (int)a0[i] : 0; A[4 + i] = aok ? (int)a1[i] : 0; }
+                for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
                 acc[mt] = mfma16x16x128_fp8_fp4(A, B, e8, acc[mt]);
               }
             } else if constexpr (WP == WP_FP4) {
@@ -357,7 +357,6 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
     #pragma unroll
                 for (int mt = 0; mt < NMT; ++mt) {
                   u32x4 av = *(const u32x4*)(arow0 + (16 * mt + ar) * AROW + (32 * g + 8 * j) * 2);
-                  if (!aok) av = u32x4{0u, 0u, 0u, 0u};
                   acc[mt] = mfma16x16x32<AF>(av, b, acc[mt]);
                 }
               }
@@ -388,7 +387,6 @@ __global__ __launch_bounds__(64 * NCB * KQ) void stream_gemm_kernel(StreamArgs a
                     av = *(const u32x4*)(arow0 + (16 * mt + ar) * AROW + (32 * g + 8 * j) * 2);
                     if constexpr (QUAD) av = a16_to_quad(av);
                   }
-                  if (!aok) av = u32x4{0u, 0u, 0u, 0u};
                   if constexpr (!RSUM) R[mt] = mfma16x16x32<MAF>(av, ones, R[mt]);
                   P[mt] = mfma16x16x32<MAF>(av, b, P[mt]);
                 }

@@ -10,9 +10,8 @@ with every (token, slot) row routed to it, over a thread pool).  The bar is the 
 small cases, max|Y - Y_ref| / max|Y_ref| over the whole tensor, with any non-finite output
 element a failure (outputs start as NaN, so an unwritten element fails too).
 
-The W4A8 MoE sweep runs twice per T: with the workspace qg_workspace_bytes asks for and with
-none, so both routes the library has for it are checked at full size.  The MoE layers at the
-end of the file check sampled tokens (their oracle needs every gate/up row of a token).
+The MoE layers at the end of the file check sampled tokens (their oracle needs every gate/up
+row of a token).
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -176,17 +175,15 @@ def test_moe_w4a16_mxfp4_e128(c4, t):
 
 @pytest.fixture(scope="module")
 def c5():
-    d = _MoE(*synth.moe_w4a8_int4(t=max(C5_T), experts=64, topk=6, n=2816, k=4096, seed=0), C5_T,
-             routes=(True, False))
+    d = _MoE(*synth.moe_w4a8_int4(t=max(C5_T), experts=64, topk=6, n=2816, k=4096, seed=0), C5_T)
     yield d
     del d
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("route", [True, False], ids=["workspace", "no_workspace"])
 @pytest.mark.parametrize("t", C5_T)
-def test_moe_w4a8_int4_e64_skewed(c5, t, route):
-    c5.check(t, route)
+def test_moe_w4a8_int4_e64_skewed(c5, t):
+    c5.check(t)
 
 
 # ---- whole MoE layers at full size ----------------------------------------------------------
@@ -298,7 +295,7 @@ def test_moe_layer_w4a4_e128_full_size(c4_layer_w4a4, t):
 def test_moe_w4a8_layer_steps_full_size(t):
     # The W4A8 layer's steps at the benchmark's launch shapes, each on generated inputs:
     # SwiGLU -> e4m3 over T*6 rows of 2*1408, the down product (E=64, N=4096, K=1408, slot
-    # rows, with the widening workspace) and the combine over N=4096.
+    # rows) and the combine over N=4096.
     from oracle import moe_layer as ML
     from oracle import formats as F
     topk, inter, hidden = 6, 1408, 4096

@@ -333,15 +333,15 @@ def test_dense_split_k_is_deterministic_and_checks_workspace():
         qg.gemm(p, x, None, y1, 96, None)
 
 
-# ---- W4A8 above the streaming sizes: both routes ---------------------------------------
-# With the workspace qg_workspace_bytes asks for, the e4m3 activations are widened to bf16
-# and the 16-bit MFMA kernel runs; without it, the e4m3 MFMA kernel with per-group promotion.
+# ---- W4A8 above the streaming sizes: int4 -> e4m3 in the MFMA kernel --------------------
+# Each 128-wide K step is one scale group: two 32x32x64 fp8 MFMAs from zero, promoted by the
+# group scale; 128- and 256-row tiles, and split K (partials summed with the per-token scale).
 
-@pytest.mark.parametrize("m", [100, 300])
-def test_dense_w4a8_without_workspace_runs_e4m3_mfma(m):
+@pytest.mark.parametrize("m", [100, 300, 700])
+def test_dense_w4a8_e4m3_mfma(m):
     layer, acts = synth.moe_w4a8_int4(t=m, experts=1, topk=1, n=320, k=1024, seed=17)
     p, buf = layers.prepare_layer(layer)
-    assert qg.workspace_bytes(p, m) == ((m * 1024 * 2 + 255) // 256) * 256
+    assert qg.workspace_bytes(p, m) == 0          # 8 K steps: no split
     x, xs = layers.acts_to_dev(acts)
     y = torch.full((m, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
     qg.gemm(p, x, xs, y, m, None)
@@ -349,10 +349,37 @@ def test_dense_w4a8_without_workspace_runs_e4m3_mfma(m):
     assert R.relative_error(layers.out_bits_to_f64(y), R.dense_reference(layer, acts)) <= TOL8
 
 
-@pytest.mark.parametrize("t", [400, 1000])
-def test_moe_w4a8_int4_widened_route(t):
+def test_dense_w4a8_e4m3_mfma_split_k():
+    # 2 x 2 output tiles of 128 x 256 and 32 K steps: K split 4 ways over workgroups
+    layer, acts = synth.moe_w4a8_int4(t=200, experts=1, topk=1, n=512, k=4096, seed=20)
+    p, buf = layers.prepare_layer(layer)
+    need = qg.workspace_bytes(p, 200)
+    assert need == 4 * 200 * 512 * 4
+    x, xs = layers.acts_to_dev(acts)
+    y = torch.full((200, 512), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
+    with pytest.raises(qg.QGError):
+        qg.gemm(p, x, xs, y, 200, None)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    qg.gemm(p, x, xs, y, 200, ws)
+    torch.cuda.synchronize()
+    assert R.relative_error(layers.out_bits_to_f64(y), R.dense_reference(layer, acts)) <= TOL8
+
+
+def test_dense_w4a8_e4m3_mfma_256_row_tiles():
+    # 3100 rows x 8192 columns: 13 x 32 tiles of 256 x 256, over 1.5 workgroups per CU
+    layer, acts = synth.moe_w4a8_int4(t=3100, experts=1, topk=1, n=8192, k=256, seed=21)
+    y = _run_dense(layer, synth.Acts(acts.x, acts.x_scale, None), 3100)
+    assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
+
+
+@pytest.mark.parametrize("t", [1200, 2100])
+def test_moe_w4a8_int4_256_row_blocks(t):
+    # 600 / 1050 rows per expert on average: 256-row blocks
     layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=18)
-    y = _run_moe(layer, acts, workspace=True)
+    p, _ = layers.prepare_layer(layer)
+    assert qg.moe_block_m(p, t, 2) == 256
+    assert qg.workspace_bytes(p, t, 2) == 0
+    y = _run_moe(layer, acts)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
 
 
