@@ -191,6 +191,21 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qg_gemm_noalloc: for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The same product,
+ * kernels and tile / split choice as qg_gemm(p, x, x_scale, y, m, ws, ws_bytes, stream),
+ * with the workspace taken from a device array of this library holding
+ * qg_noalloc_scratch_bytes() = 32 MiB, one per GPU, kept until the process ends.  No call
+ * allocates or frees memory.  Every dense split over K the selector makes fits (at most
+ * 32 MiB of partials); a workspace beyond the array would be QG_ERR_WORKSPACE before any
+ * launch.  Nothing in the array must start at zero: each call writes what it reads.  All calls on one GPU share its array, so calls that overlap on that GPU
+ * (concurrent streams, or host threads) race and give wrong results: serialise them.
+ */
+qg_status qg_gemm_noalloc(const qg_prepared* p, const void* x, const void* x_scale, void* y, int64_t m,
+                          void* stream);
+size_t qg_noalloc_scratch_bytes(void);
+
+/*
  * MoE routing preparation (the indexed input path: rows are gathered through
  * routing indices).  qg_moe_block_m returns the row-block size the grouped GEMM
  * will use for T tokens with topk slots (0 on an invalid handle).

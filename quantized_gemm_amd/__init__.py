@@ -31,6 +31,7 @@ STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_E
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
            "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine",
            "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_ceiling_read", "qg_ceiling_mfma",
+           "qg_gemm_noalloc", "qg_noalloc_scratch_bytes",
            "qg_status_str", "qg_version"]
 
 
@@ -88,6 +89,8 @@ def lib():
         L.qg_quantize_e4m3_rows.restype = i32
         L.qg_dequant.argtypes, L.qg_dequant.restype = [pp, i32, vp, vp], i32
         u64 = ctypes.c_uint64
+        L.qg_gemm_noalloc.argtypes, L.qg_gemm_noalloc.restype = [pp, vp, vp, vp, i64, vp], i32
+        L.qg_noalloc_scratch_bytes.argtypes, L.qg_noalloc_scratch_bytes.restype = [], sz
         L.qg_ceiling_read.argtypes, L.qg_ceiling_read.restype = [vp, u64, i32, vp, u64, vp], i32
         L.qg_ceiling_mfma.argtypes, L.qg_ceiling_mfma.restype = [i32, i64, i32, vp, u64, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
@@ -152,6 +155,16 @@ def gemm(p: Prepared, x, x_scale, y, m: int, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().qg_gemm(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(y), m, _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "qg_gemm")
+
+
+def gemm_noalloc(p: Prepared, x, x_scale, y, m: int, stream=None):
+    """qg_gemm with the library's own per-GPU scratch array as the workspace (no allocation)."""
+    st = lib().qg_gemm_noalloc(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(y), m, _stream(stream))
+    _check(st, "qg_gemm_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return lib().qg_noalloc_scratch_bytes()
 
 
 def moe_block_m(p: Prepared, tokens: int, topk: int) -> int:
