@@ -449,6 +449,23 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
   u32x4 Bq[2][NT];
   if constexpr (!F8) dequant(bw[0], 0, scl[0], zsl[0], Bq[0]);
+  // int4 -> e4m3: unit u of the lane (32 K, QUAD order) -> the 32 e4m3 bytes of MFMA u's B
+  // operand, in k order.  Step 0's units are converted here; each later step's during the
+  // step before it, one word per row tile between the MFMAs.
+  i32x8 Bc[NT][2];
+  auto cvt_word = [&](const u32x4 (&src)[NT][BU], int t, int u, int j, i32x8 (&dst)[NT][2]) {
+    const u32x2 e = int4q_to_e4m3(src[t][u][j]);
+    dst[t][u][2 * j] = (int)e[0];
+    dst[t][u][2 * j + 1] = (int)e[1];
+  };
+  if constexpr (I4F8) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cvt_word(bw[0], t, u, j, Bc);
+  }
 
   // One K step; S = step % 3 is a compile-time stage index (the loop below is unrolled
   // by three), so every LDS address names its stage array.
@@ -541,21 +558,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (I4F8) {
-      // int4 -> e4m3 (exact, a byte table per 4 weights): each of the lane's two units
-      // (32 K of its column, QUAD order) becomes the 32-byte e4m3 operand of one 32x32x64
-      // MFMA, in k order; the activation operand is the same 32 K of the row (chunks 4j + 2g
-      // and 4j + 2g + 1 of the row segment), so both sides share one k order.
-      i32x8 Bc[NT][2];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x2 e = int4q_to_e4m3(b0[t][u][j]);
-            Bc[t][u][2 * j] = (int)e[0];
-            Bc[t][u][2 * j + 1] = (int)e[1];
-          }
+      // The lane's two units of this step were converted during the previous step (Bc): each
+      // is the 32-byte e4m3 B operand of one 32x32x64 MFMA (k = 64u + 32g .. of the step, in k
+      // order); the activation operand is the same 32 K of the row (chunks 4u + 2g and
+      // 4u + 2g + 1 of the row segment), so both sides share one k order.
       auto read_a8i = [&](int mt, int j) -> i32x8 {
         const int row = 32 * mt + r;
         const int lc0 = 4 * j + 2 * g;
@@ -569,13 +575,22 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // The step is one scale group: each row tile's product P over the step's 128 K starts
       // from zero (two MFMAs) and is promoted, acc += s * P, one row tile behind, so that the
       // promotion of tile mt - 1 runs while the MFMAs of tile mt do; activation fragments
-      // (q = 2 mt + j) are read one MFMA ahead.
+      // (q = 2 mt + j) are read one MFMA ahead.  Between them the next step's weights are
+      // converted, NT * 8 / MT words per row tile (the step's VALU work spread over its MFMAs
+      // instead of a burst after the barrier, when both waves of a SIMD would convert at once).
       const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      constexpr int NWD = NT * 8;                      // words to convert per step
+      constexpr int WPM = (NWD + MT - 1) / MT;         // words per row tile
+      // 128-row tiles promote one row tile behind (two product buffers); 256-row tiles have no
+      // registers for a second buffer and promote each tile right after its MFMAs, the
+      // conversion words in between covering part of the MFMA latency
+      constexpr int LAG = BM == 256 ? 0 : 1;
+      i32x8 Bn[NT][2];
       i32x8 Ai[2];
-      f32x16 P[2][NT];
+      f32x16 P[LAG + 1][NT];
       Ai[0] = read_a8i(0, 0);
 #pragma unroll
-      for (int mt = 0; mt <= MT; ++mt) {
+      for (int mt = 0; mt < MT + LAG; ++mt) {
         if (mt < MT) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -583,19 +598,30 @@ void mfma_gemm_kernel(MfmaArgs a) {
             if (q + 1 < 2 * MT) Ai[(q + 1) & 1] = read_a8i((q + 1) >> 1, (q + 1) & 1);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-              P[mt & 1][t] = mfma32x32x64_fp8(Ai[q & 1], Bc[t][j], j == 0 ? zero16 : P[mt & 1][t]);
+              P[mt % (LAG + 1)][t] = mfma32x32x64_fp8(Ai[q & 1], Bc[t][j], j == 0 ? zero16 : P[mt % (LAG + 1)][t]);
+          }
+#pragma unroll
+          for (int w = 0; w < WPM; ++w) {
+            const int wd = mt * WPM + w;
+            if (wd < NWD) cvt_word(b1, wd / 8, (wd / 4) & 1, wd & 3, Bn);
           }
         }
-        if (mt > 0) {
+        const int pm = mt - LAG;                       // row tile promoted now
+        if (pm >= 0) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              acc[mt - 1][t][i] = __builtin_fmaf(scl[S][t], P[(mt - 1) & 1][t][i], acc[mt - 1][t][i]);
-            keep_in_vgprs(acc[mt - 1][t]);
+              acc[pm][t][i] = __builtin_fmaf(scl[S][t], P[pm % (LAG + 1)][t][i], acc[pm][t][i]);
+            keep_in_vgprs(acc[pm][t]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        Bc[t][0] = Bn[t][0];
+        Bc[t][1] = Bn[t][1];
       }
     } else if constexpr (F8) {
       // 2 x MT MFMA pairs per step (k halves j, row tiles mt); each pair's activation
