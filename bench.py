@@ -138,6 +138,20 @@ def measure_ceilings(args):
         s = e0.elapsed_time(e1) * 1e-3
         out["mfma_tflops"][names[dt]] = round(wgs * 4 * iters * 4 * flop_per[dt] / s / 1e12, 1)
     out["mfma_tflops"]["f16"] = out["mfma_tflops"]["bf16"]
+    # LDS reads: one workgroup of 8 waves per CU, 16 bytes per lane per read
+    lwg, liters = 256, 20000
+    lsink = torch.empty(lwg * 512, dtype=torch.int32, device="cuda")
+    qg.ceiling_lds(100, lwg, lsink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    qg.ceiling_lds(liters, lwg, lsink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3
+    lds_bytes = lwg * 512 * liters * 8 * 16
+    out["lds_read_TBps"] = round(lds_bytes / s / 1e12, 2)
+    out["lds_read_bytes_per_clk_per_cu_at_2.4GHz"] = round(lds_bytes / s / 256 / 2.4e9, 1)
     out["method"] = ("read: qg_ceiling_read, best of 2/4/8/16 16-byte loads per lane, back-to-back launches "
                      "between HIP events over buffers rotated through 1 GiB; mfma: qg_ceiling_mfma, 512 "
                      "workgroups x 4 waves x 4 independent 32x32 MFMAs per iteration")

@@ -394,6 +394,9 @@ qg_status qg_ceiling_read(const void* buf, uint64_t bytes, int32_t loads_per_lan
                           uint64_t sink_words, void* stream);
 qg_status qg_ceiling_mfma(int32_t dtype, int64_t iters, int32_t workgroups, float* sink, uint64_t sink_floats,
                           void* stream);
+/* qg_ceiling_lds: `workgroups` workgroups of 8 waves, each lane reading iters x 8 x 16 bytes
+ * of its CU's LDS (64 KiB, conflict-free addresses); sink device uint32 [workgroups * 512]. */
+qg_status qg_ceiling_lds(int64_t iters, int32_t workgroups, uint32_t* sink, uint64_t sink_words, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* qg_status_str(qg_status s);

@@ -30,7 +30,7 @@ STATUS = {0: "QG_OK", 1: "QG_ERR_INVALID_ARG", 2: "QG_ERR_UNSUPPORTED", 3: "QG_E
           4: "QG_ERR_NOT_PREPARED", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_CAPACITY", 7: "QG_ERR_HIP"}
 EXPORTS = ["qg_prepared_bytes", "qg_prepare", "qg_workspace_bytes", "qg_gemm", "qg_moe_block_m", "qg_moe_capacity",
            "qg_moe_align", "qg_moe_grouped_map", "qg_moe_gemm", "qg_moe_swiglu", "qg_moe_combine",
-           "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_ceiling_read", "qg_ceiling_mfma",
+           "qg_quantize_e4m3_rows", "qg_quantize_e2m1_rows", "qg_dequant", "qg_ceiling_read", "qg_ceiling_mfma", "qg_ceiling_lds",
            "qg_gemm_noalloc", "qg_noalloc_scratch_bytes",
            "qg_status_str", "qg_version"]
 
@@ -93,6 +93,7 @@ def lib():
         L.qg_noalloc_scratch_bytes.argtypes, L.qg_noalloc_scratch_bytes.restype = [], sz
         L.qg_ceiling_read.argtypes, L.qg_ceiling_read.restype = [vp, u64, i32, vp, u64, vp], i32
         L.qg_ceiling_mfma.argtypes, L.qg_ceiling_mfma.restype = [i32, i64, i32, vp, u64, vp], i32
+        L.qg_ceiling_lds.argtypes, L.qg_ceiling_lds.restype = [i64, i32, vp, u64, vp], i32
         L.qg_status_str.argtypes, L.qg_status_str.restype = [i32], ctypes.c_char_p
         L.qg_version.argtypes, L.qg_version.restype = [], i32
         _lib = L
@@ -244,3 +245,7 @@ def ceiling_mfma(dtype: int, iters: int, workgroups: int, sink, stream=None):
     _check(lib().qg_ceiling_mfma(dtype, iters, workgroups, _ptr(sink), sink.numel(), _stream(stream)),
            "qg_ceiling_mfma")
 
+
+def ceiling_lds(iters: int, workgroups: int, sink, stream=None):
+    """Measurement helper: conflict-free 16-byte LDS reads by 8 waves per workgroup (see qg_ceiling_lds)."""
+    _check(lib().qg_ceiling_lds(iters, workgroups, _ptr(sink), sink.numel(), _stream(stream)), "qg_ceiling_lds")

@@ -4,7 +4,9 @@
 //    16-byte loads, every lane's loads issued before any is used (the access pattern of
 //    the weight stream), reduced to one word per wave so the loads cannot be dropped;
 //  * MFMA loop: the rate of back-to-back independent MFMAs of one type with operands in
-//    registers, two waves per SIMD, nothing else in the loop.
+//    registers, two waves per SIMD, nothing else in the loop;
+//  * LDS reads: the rate at which 8 waves of a workgroup read their CU's LDS with
+//    conflict-free 16-byte reads.
 //
 // Neither computes anything of the GEMM; both exist so that a kernel's time can be read
 // against what the memory system and the matrix cores deliver on the same box.
@@ -76,6 +78,25 @@ __global__ __launch_bounds__(256) void ceiling_mfma_kernel(int64_t iters, float*
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// LDS reads: 8 waves per workgroup, each lane reading 16 bytes per instruction at
+// consecutive addresses (conflict-free), eight instructions in flight per lane.
+__global__ __launch_bounds__(512) void ceiling_lds_kernel(int64_t iters, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[65536];
+  for (int i = threadIdx.x; i < 65536 / 16; i += 512) *(u32x4*)(buf + 16 * i) = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane_off = (threadIdx.x & 63) * 16 + (threadIdx.x >> 6) * 8192;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (int64_t it = 0; it < iters; ++it) {
+    const int base = (int)((it * 1024) & 8191);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const u32x4 v = *(const u32x4*)(buf + ((lane_off + base + u * 1024 * 8) & 65535));
+      x ^= v;
+    }
+  }
+  sink[blockIdx.x * 512 + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
 }  // namespace qg
 
 using namespace qg;
@@ -111,6 +132,13 @@ qg_status qg_ceiling_mfma(int32_t dtype, int64_t iters, int32_t workgroups, floa
   if (dtype == 0) hipLaunchKernelGGL(ceiling_mfma_kernel<0>, dim3(workgroups), dim3(256), 0, st, iters, sink);
   else if (dtype == 1) hipLaunchKernelGGL(ceiling_mfma_kernel<1>, dim3(workgroups), dim3(256), 0, st, iters, sink);
   else hipLaunchKernelGGL(ceiling_mfma_kernel<2>, dim3(workgroups), dim3(256), 0, st, iters, sink);
+  return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_HIP;
+}
+
+qg_status qg_ceiling_lds(int64_t iters, int32_t workgroups, uint32_t* sink, uint64_t sink_words, void* stream) {
+  if (iters <= 0 || workgroups <= 0 || !sink) return QG_ERR_INVALID_ARG;
+  if (sink_words < (uint64_t)workgroups * 512) return QG_ERR_WORKSPACE;
+  hipLaunchKernelGGL(ceiling_lds_kernel, dim3(workgroups), dim3(512), 0, (hipStream_t)stream, iters, sink);
   return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_HIP;
 }
 
