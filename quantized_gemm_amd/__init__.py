@@ -158,6 +158,21 @@ def gemm(p: Prepared, x, x_scale, y, m: int, ws=None, stream=None):
     _check(st, "qg_gemm")
 
 
+def gemm_call(p: Prepared, x, x_scale, y, m: int, ws=None, stream=None):
+    """qg_gemm with every argument converted once: returns a no-argument callable that enqueues
+    the same launch again (for timing loops, where per-call tensor slicing and stream lookup
+    would cost more host time than a small kernel takes on the GPU)."""
+    fn = lib().qg_gemm
+    args = (ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(y), m, _ptr(ws),
+            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise QGError(st, "qg_gemm")
+    return call
+
+
 def gemm_noalloc(p: Prepared, x, x_scale, y, m: int, stream=None):
     """qg_gemm with the library's own per-GPU scratch array as the workspace (no allocation)."""
     st = lib().qg_gemm_noalloc(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(y), m, _stream(stream))
@@ -201,6 +216,20 @@ def moe_gemm(p: Prepared, x, x_scale, sorted_ids, expert_ids, num_post_pad, toke
     st = lib().qg_moe_gemm(ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(sorted_ids), _ptr(expert_ids),
                            _ptr(num_post_pad), tokens, topk, block_m, _ptr(y), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "qg_moe_gemm")
+
+
+def moe_gemm_call(p: Prepared, x, x_scale, sorted_ids, expert_ids, num_post_pad, tokens: int, topk: int,
+                  block_m: int, y, ws=None, stream=None):
+    """qg_moe_gemm with every argument converted once (see gemm_call)."""
+    fn = lib().qg_moe_gemm
+    args = (ctypes.byref(p), _ptr(x), _ptr(x_scale), _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_pad), tokens,
+            topk, block_m, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise QGError(st, "qg_moe_gemm")
+    return call
 
 
 def moe_swiglu(gate_up, rows: int, inter: int, in_type: int, out_type: int, out, out_scale=None, stream=None):
