@@ -202,9 +202,20 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // step t (k = 64t + 32h ..): e2m1 blocks of 32, two per step; int4 groups are a
   // multiple of 128 (or the whole K), so both halves share one (a wave-uniform division).
   constexpr int ES = ST == S_UE8M0 ? 1 : 2;               // bytes per stored scale
+  // int4 scale group of step t = (kstep0 + t) / gsteps, steps per group gsteps (the whole K,
+  // group 0, is one group), as a multiply-high by grec = ceil(2^32 / gsteps): exact for
+  // step indices and divisors below 2^16 (the error term x (grec gsteps - 2^32) / 2^32 stays
+  // below 1 / gsteps), and for any power-of-two divisor (no error term); no division in the loop
+  // (gsteps 1: grec 0 and gone 1, the quotient is x itself)
+  const uint32_t gsteps = a.group == 0 ? (1u << 30) : (uint32_t)max(1, a.group / BK);
+  const uint32_t grec = gsteps == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + gsteps - 1) / gsteps);
+  const uint32_t gone = gsteps == 1 ? 1u : 0u;
   auto group_of = [&](int t, int h) -> int {
     if constexpr (WP == WP_FP4) return (kstep0 + t) * 2 + h;
-    else return a.group == 0 ? 0 : ((kstep0 + t) * BK) / a.group;
+    else {
+      const uint32_t x = (uint32_t)(kstep0 + t);
+      return (int)(__umulhi(x, grec) + x * gone);
+    }
   };
   // scale lane -> K half, 16-column block of the tile, 16-byte part of the block's 16 scales
   const int s_h = lane / (16 * ES), s_nb = (lane % (16 * ES)) / ES, s_part = lane % ES;
@@ -217,13 +228,22 @@ void mfma_gemm_kernel(MfmaArgs a) {
       make_rsrc(ZERO ? (const void*)(a.z + sc_expert * 2) : a.s, ZERO ? (uint32_t)(nb_count * ngroups * 8) : 0u);
   // Step t's records into region reg: scales of half h at reg + 256 ES h + 16 ES nb + ES c;
   // the two zero words of the step's group (and the next group's) at reg + 1024 + 16 nb.
+  // Wave 0 loads the scales, wave 1 the zero words: the wave's source, destination, lane
+  // offset and bytes per group are chosen once here, so each step costs one wave-uniform
+  // branch and one load.
+  const bool sz_wave = SDMA && (wave == 0 || (ZERO && wave == 1));
+  const bool sz_zero = ZERO && wave == 1;
+  const __amdgpu_buffer_rsrc_t szr = sz_zero ? zr : sr;
+  const int sz_dst = sz_zero ? 1024 : 0;
+  const bool sz_ok = sz_zero ? z_ok : s_ok;
+  const int sz_h = sz_zero ? 0 : s_h;
+  const int sz_base = sz_zero ? (ntile * 16 + lane) * ngroups * 8 : (ntile * 16 + s_nb) * ngroups * 16 * ES + 16 * s_part;
+  const int sz_gb = sz_zero ? 8 : 16 * ES;                          // bytes per group
   auto issue_sz = [&](int t, uint8_t* reg) {
     if constexpr (SDMA) {
-      if (wave == 0) {
-        bload16_lds(sr, reg, s_ok && t < nsteps ? ((ntile * 16 + s_nb) * ngroups + group_of(t, s_h)) * 16 * ES + 16 * s_part
-                                                : kOOB);
-      } else if (ZERO && wave == 1) {
-        bload16_lds(zr, reg + 1024, z_ok && t < nsteps ? ((ntile * 16 + lane) * ngroups + group_of(t, 0)) * 8 : kOOB);
+      if (sz_wave) {
+        const int off = sz_base + group_of(t, sz_h) * sz_gb;
+        bload16_lds(szr, reg + sz_dst, ((t < nsteps) && sz_ok) ? off : kOOB);
       }
     }
   };
@@ -310,11 +330,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
         zs[t] = 0.f;
       } else if constexpr (I4F8) {
         // one step (128 K) lies inside one scale group: the step's products are promoted by it
-        const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
+        const int gi = group_of(step, 0);
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         zs[t] = 0.f;
       } else if constexpr (WP == WP_INT4_MAGIC) {
-        const int gi = a.group == 0 ? 0 : ((kstep0 + step) * BK) / a.group;
+        const int gi = group_of(step, 0);
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
         float z = 8.0f;
         if constexpr (ZERO) {
