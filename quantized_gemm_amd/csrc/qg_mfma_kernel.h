@@ -365,12 +365,14 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
   // idle and its registers free for other values.  Vector-memory issue order, kept by
   // sched_barrier: [B(0)] R(1) A(0) B(DIST-2) R(2) A(1) B(DIST-1), then per step s R(s+3)
-  // and A(s+2) (e4m3: at the top; 16-bit: R at the top, A one piece per sub-step) and
-  // B(s+DIST) at the bottom (DIST = 3) or right after A(s+2) (DIST = 2).  R(t) are the scale / zero records of step t (16-bit paths; one load on
-  // waves 0 and 1 only), issued with A(t-1) into that stage's region, so they land when
-  // A(t-1) does and are read at the top of step t-1.  At the top of step s the loads
-  // issued after A(s) include at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <=
-  // APT + 2*NB means A(s) has landed; the record loads only make that count larger.
+  // and A(s+2) (e4m3: at the top; 16-bit: in sub-steps 2 and 3, after the mid-step
+  // barrier) and B(s+DIST) at the bottom (DIST = 3) or right after A(s+2) (DIST = 2).
+  // R(t) are the scale / zero records of step t (16-bit paths; one load on waves 0 and 1
+  // only), issued with A(t-1) into that stage's region, so they land when A(t-1) does and
+  // are read at the top of step t-1.  Where a stage is published (the top of its step for
+  // e4m3, before the loop for the first 16-bit stage), the loads issued after A(s) include
+  // at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <= APT + 2*NB means A(s) has
+  // landed; the record loads only make that count larger.
   constexpr int DIST = F8 ? 2 : 3;
   u32x4 bw[3][NT][BU];
   float scl[3][NT], zsl[3][NT];
@@ -469,6 +471,16 @@ void mfma_gemm_kernel(MfmaArgs a) {
 
   u32x4 Bq[2][NT];
   if constexpr (!F8) dequant(bw[0], 0, scl[0], zsl[0], Bq[0]);
+  // 16-bit paths publish a stage in the middle of the step before it (below), so the
+  // first step's stage is published here and its first fragments read before the loop
+  u32x4 Af[MT];   // one fragment register set per row tile (16-bit path)
+  if constexpr (!F8) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_A & 15) | ((VM_A >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_a16(sA0, 0, Af);
+  }
   // int4 -> e4m3: unit u of the lane (32 K, QUAD order) -> the 32 e4m3 bytes of MFMA u's B
   // operand, in k order.  Step 0's units are converted here; each later step's during the
   // step before it, one word per row tile between the MFMAs.
@@ -498,22 +510,20 @@ void mfma_gemm_kernel(MfmaArgs a) {
     uint8_t* const sXn = S == 0 ? sX2 : S == 1 ? sX0 : sX1;   // exponents of step + 2
     constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
     uint8_t* const sSn = S == 0 ? sS2 : S == 1 ? sS0 : sS1;
-    // this wave's A(step) loads have landed; the barrier makes every wave's visible and
-    // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_A & 15) | ((VM_A >> 4) << 14));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // 16-bit: the first sub-step's activation fragments and the next step's scales are
-    // read before the new loads go out, so that the first MFMAs wait only for them
-    u32x4 Af[MT];   // one fragment register set per row tile (16-bit path)
-    uint32_t sbits[NT], zbits[NT];
-    if constexpr (!F8) {
-      read_a16(sAb, 0, Af);
-      read_sz(sSb, sbits, zbits);
+    const uint8_t* const sA1b = S == 0 ? sA1 : S == 1 ? sA2 : sA0;   // stage of step + 1
+    if constexpr (F8) {
+      // this wave's A(step) loads have landed; the barrier makes every wave's visible and
+      // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_A & 15) | ((VM_A >> 4) << 14));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
+    // 16-bit: the next step's scale and zero words (published with this step's stage)
+    uint32_t sbits[NT], zbits[NT];
+    if constexpr (!F8) read_sz(sSb, sbits, zbits);
     __builtin_amdgcn_sched_barrier(0);
-    issue_sz(step + 3, sSn);
+    if constexpr (F8) issue_sz(step + 3, sSn);   // 16-bit: after the mid-step barrier, below
     issue_xs(step + 2, sXn);
     if constexpr (F8) issue_a(step + 2, sAn);   // 16-bit: one piece per sub-step, below
     __builtin_amdgcn_sched_barrier(0);
@@ -698,25 +708,42 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // Software pipeline over the 4 sub-steps, ordered by hand: after the two MFMAs of
       // each row tile come one stage of the next sub-step's dequantization and that tile's
       // next activation fragment read; sched_barrier keeps the order.  Sub-step 3
-      // dequantizes sub-step 0 of the next step (its weights and scales are in registers).
-      // a row tile's next fragment is read into its register set right after its MFMAs,
-      // one sub-step (MT * NT MFMAs) ahead of use
+      // dequantizes sub-step 0 of the next step (its weights and scales are in registers)
+      // and reads its fragments from the next stage.  A row tile's next fragment is read
+      // into its register set right after its MFMAs, one sub-step (MT * NT MFMAs) ahead.
+      //
+      // Stage hand-over in the middle of the step, so that no MFMA waits for an LDS read
+      // issued after a barrier: after sub-step 1 every wave waits for its own A(step + 1)
+      // loads (issued during step - 1; after them it issued only B(step + 2), NB loads)
+      // and passes the barrier.  Past it, A(step + 1) is visible to every wave (sub-step 3
+      // reads it), and every wave has finished step - 1, the last reader of the stage
+      // and record region that A(step + 2) and R(step + 3) then overwrite (sub-steps 2
+      // and 3, records first, so that they land no later than the stage they ride with).
       constexpr int PH = NT * 4;                 // dequant stages per sub-step
       constexpr int PPM = (PH + MT - 1) / MT;    // stages after each row tile
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool last = (j == 3);
         DQ dq[NT];
+        if (j == 2) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (NB & 15) | ((NB >> 4) << 14));
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[mt], Bq[j & 1][t], acc[mt][t]);
-          // A(step + 2) goes out in pieces spread over the sub-steps (measured ~2% faster
-          // than all at the top); every piece precedes B(step + 3), as the waits assume
-          if (mt == 0) {
+          // R(step + 3) and A(step + 2) go out in sub-steps 2 and 3, the pieces spread over
+          // both; every piece precedes B(step + 3), as the waits assume
+          if (mt == 0 && j >= 2) {
+            if (j == 2) issue_sz(step + 3, sSn);
 #pragma unroll
             for (int i = 0; i < APT; ++i)
-              if ((i * 4) / APT == j) issue_a_piece(step + 2, sAn, i);
+              if ((i * 2) / APT == j - 2) issue_a_piece(step + 2, sAn, i);
           }
 #pragma unroll
           for (int q = 0; q < PPM; ++q) {
@@ -727,9 +754,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
               else dq_stage(b0, j + 1, t, stg, scl[S], zsl[S], dq[t], Bq[(j + 1) & 1][t]);
             }
           }
-          if (!last) {
+          {
             const int row = 32 * mt + r;
-            Af[mt] = *(const u32x4*)(sAb + row * ROWB + 16 * ((4 * g + j + 1) ^ ((row >> 1) & 7)));
+            const uint8_t* const src = last ? sA1b : sAb;
+            Af[mt] = *(const u32x4*)(src + row * ROWB + 16 * ((4 * g + ((j + 1) & 3)) ^ ((row >> 1) & 7)));
           }
           if (j == 0 && mt == MT - 1) {
             // the raw words are taken as they are here, so no conversion moves up to
