@@ -397,6 +397,37 @@ def test_dense_streaming_split_needs_workspace():
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL16
 
 
+def test_dense_split_graph_replays():
+    # A captured split-K call (16 rows: weight streaming over 8 K slices, then the slice
+    # reduction) replayed with alternating activations, with eager work and synchronisations
+    # between the replays; every replay must match the oracle.
+    layer, acts_a = synth.dense_w4a16_asym_bf16(m=16, n=2048, k=4096, seed=23)
+    acts_b = synth.dense_w4a16_asym_bf16(m=16, n=2048, k=4096, seed=24)[1]
+    p, buf = layers.prepare_layer(layer)
+    xa, _ = layers.acts_to_dev(acts_a)
+    xb, _ = layers.acts_to_dev(acts_b)
+    ref_a, ref_b = R.dense_reference(layer, acts_a), R.dense_reference(layer, acts_b)
+    ws = torch.zeros(qg.workspace_bytes(p, 16), dtype=torch.uint8, device="cuda")
+    xs = xa.clone()
+    y = torch.empty((16, 2048), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qg.gemm(p, xs, None, y, 16, ws, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qg.gemm(p, xs, None, y, 16, ws, stream=s)
+    torch.cuda.synchronize()
+    for xi, ref in [(xb, ref_b), (xa, ref_a), (xb, ref_b), (xa, ref_a)]:
+        xs.copy_(xi)
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert R.relative_error(layers.out_bits_to_f64(y), ref) <= TOL16
+
+
 @pytest.mark.parametrize("name", ["asym_g0_n320", "sym_g384", "fp8_block", "mxfp4_n192"])
 def test_prepare_writes_every_byte_of_the_image(name):
     # regions whose sizes are not multiples of 256 bytes: the padding up to the next region
