@@ -52,7 +52,10 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int BN = 256;
   constexpr int ROWB = 128;
   constexpr int STAGE = BM * ROWB;
-  constexpr int NS = 3;                      // activation stages in LDS (ring)
+  // activation stages in LDS (ring): 16-bit paths 4 (the stage three steps ahead is loaded
+  // after the mid-step hand-over, so its loads get two steps to land), byte paths 3
+  constexpr int NS = F8 ? 3 : 4;
+  constexpr int AHEAD = NS - 1;              // steps between a stage's loads and its use
   constexpr int APT = STAGE / 16 / NTHR;     // 16-byte activation pieces per thread per step
   constexpr int BU = F8 ? ((FP4B || I4F8) ? 2 : 4) : 1;   // 16-byte weight units per lane per tile and step (F4A: 4)
   // elements held by the bytes of the low / high nibble words of a 4-bit code word (PAIR order)
@@ -64,6 +67,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sA0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sA1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sA2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sA3[NS == 4 ? STAGE : 16];
   // 16-bit paths: the next step's scale (and zero) records of the tile's 256 columns,
   // one region per activation stage, loaded HBM -> LDS with that stage's activations
   // (scales in the first KiB, zero words in the second)
@@ -72,6 +76,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sS0[SREG];
   __shared__ __attribute__((aligned(16))) uint8_t sS1[SREG];
   __shared__ __attribute__((aligned(16))) uint8_t sS2[SREG];
+  __shared__ __attribute__((aligned(16))) uint8_t sS3[NS == 4 ? SREG : 16];
   // e2m1 activations: the step's UE8M0 exponents of each tile row (8 bytes: K groups
   // 8 step .. 8 step + 7), one region per activation stage, loaded with that stage
   constexpr int XSB = F4A ? BM * 8 : 16;
@@ -359,7 +364,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
       for (int i = 0; i < 16; ++i) acc[mt][t][i] = 0.f;
 
   // ---- prologue: A(0), A(1) -> LDS stages 0, 1; weights and scales -------------------
-  // Weights and scales live in a ring of three register sets, slot = step % 3 (a
+  // Weights and scales live in a ring of NS register sets, slot = step % NS (a
   // compile-time index in the unrolled loop), loaded DIST steps ahead.  16-bit
   // activations: DIST = 3, since the last sub-step of step s already dequantizes step
   // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
@@ -374,8 +379,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // at least B(s+DIST-2), A(s+1) and B(s+DIST-1), so vmcnt <= APT + 2*NB means A(s) has
   // landed; the record loads only make that count larger.
   constexpr int DIST = F8 ? 2 : 3;
-  u32x4 bw[3][NT][BU];
-  float scl[3][NT], zsl[3][NT];
+  u32x4 bw[NS][NT][BU];
+  float scl[NS][NT], zsl[NS][NT];
   if constexpr (DIST == 3) {
     load_b(0, bw[0]);
     load_scale(0, scl[0], zsl[0]);           // later steps' scales come through LDS
@@ -393,6 +398,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
   issue_a(1, sA1);
   __builtin_amdgcn_sched_barrier(0);
   load_b(DIST - 1, bw[DIST - 1]);
+  if constexpr (NS == 4) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_sz(3, sS2);
+    issue_a(2, sA2);
+  }
   if constexpr (F8) load_scale(min(DIST - 1, nsteps - 1), scl[DIST - 1], zsl[DIST - 1]);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int NB = NT * BU;                // weight loads per thread per step
@@ -499,18 +509,21 @@ void mfma_gemm_kernel(MfmaArgs a) {
         for (int j = 0; j < 4; ++j) cvt_word(bw[0], t, u, j, Bc);
   }
 
-  // One K step; S = step % 3 is a compile-time stage index (the loop below is unrolled
-  // by three), so every LDS address names its stage array.
+  // One K step; S = step % NS is a compile-time stage index (the loop below is unrolled
+  // by NS), so every LDS address names its stage array.
+  auto stA = [&](int i) -> uint8_t* { return i == 0 ? sA0 : i == 1 ? sA1 : i == 2 ? sA2 : sA3; };
+  auto stS = [&](int i) -> uint8_t* { return i == 0 ? sS0 : i == 1 ? sS1 : i == 2 ? sS2 : sS3; };
   auto step_body = [&](const int step, auto S_) __attribute__((always_inline)) {
     constexpr int S = decltype(S_)::value;
-    uint8_t* const sAb = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
-    uint8_t* const sAn = S == 0 ? sA2 : S == 1 ? sA0 : sA1;   // stage of step + 2
-    const uint8_t* const sSb = S == 0 ? sS0 : S == 1 ? sS1 : sS2;
+    constexpr int SN = (S + AHEAD) % NS;                      // stage of step + AHEAD
+    uint8_t* const sAb = stA(S);
+    uint8_t* const sAn = stA(SN);
+    const uint8_t* const sSb = stS(S);
     const uint8_t* const sXb = S == 0 ? sX0 : S == 1 ? sX1 : sX2;
-    uint8_t* const sXn = S == 0 ? sX2 : S == 1 ? sX0 : sX1;   // exponents of step + 2
-    constexpr int S1 = S == 2 ? 0 : S + 1;                    // slot of step + 1
-    uint8_t* const sSn = S == 0 ? sS2 : S == 1 ? sS0 : sS1;
-    const uint8_t* const sA1b = S == 0 ? sA1 : S == 1 ? sA2 : sA0;   // stage of step + 1
+    uint8_t* const sXn = S == 0 ? sX2 : S == 1 ? sX0 : sX1;   // exponents of step + 2 (3 stages)
+    constexpr int S1 = (S + 1) % NS;                          // slot of step + 1
+    uint8_t* const sSn = stS(SN);
+    const uint8_t* const sA1b = stA(S1);                      // stage of step + 1
     if constexpr (F8) {
       // this wave's A(step) loads have landed; the barrier makes every wave's visible and
       // frees the stage read during step-1 for A(step+2).  No fence: nothing else is shared.
@@ -523,11 +536,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
     uint32_t sbits[NT], zbits[NT];
     if constexpr (!F8) read_sz(sSb, sbits, zbits);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (F8) issue_sz(step + 3, sSn);   // 16-bit: after the mid-step barrier, below
+    if constexpr (F8) issue_sz(step + AHEAD + 1, sSn);   // 16-bit: after the mid-step barrier, below
     issue_xs(step + 2, sXn);
-    if constexpr (F8) issue_a(step + 2, sAn);   // 16-bit: one piece per sub-step, below
+    if constexpr (F8) issue_a(step + AHEAD, sAn);   // 16-bit: in sub-steps 2 and 3, below
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int SL = (S + DIST) % 3;                        // slot of step + DIST
+    constexpr int SL = (S + DIST) % NS;                       // slot of step + DIST
     if constexpr (DIST == 2) {
       // e4m3 weights: the slot of step + 2 (last read in step - 1) is free already, so
       // its loads go out here, two full steps ahead of use, right after A(step + 2)
@@ -714,11 +727,11 @@ void mfma_gemm_kernel(MfmaArgs a) {
       //
       // Stage hand-over in the middle of the step, so that no MFMA waits for an LDS read
       // issued after a barrier: after sub-step 1 every wave waits for its own A(step + 1)
-      // loads (issued during step - 1; after them it issued only B(step + 2), NB loads)
-      // and passes the barrier.  Past it, A(step + 1) is visible to every wave (sub-step 3
-      // reads it), and every wave has finished step - 1, the last reader of the stage
-      // and record region that A(step + 2) and R(step + 3) then overwrite (sub-steps 2
-      // and 3, records first, so that they land no later than the stage they ride with).
+      // loads and passes the barrier.  Past it, A(step + 1) is visible to every wave
+      // (sub-step 3 reads it), and every wave has finished step - 1, the last reader of the
+      // stage and record region that A(step + AHEAD) and R(step + AHEAD + 1) then
+      // overwrite (sub-steps 2 and 3, records first, so that they land no later than the
+      // stage they ride with).  With four stages a stage's loads have two steps to land.
       constexpr int PH = NT * 4;                 // dequant stages per sub-step
       constexpr int PPM = (PH + MT - 1) / MT;    // stages after each row tile
 #pragma unroll
@@ -726,8 +739,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
         const bool last = (j == 3);
         DQ dq[NT];
         if (j == 2) {
+          // loads this wave issued after its share of the next stage, at least: 3 stages
+          // B(step + 2) (NB); 4 stages the stage after it and one step of weights (APT + NB:
+          // B(2) and A(2) of the prologue for step 0, A(3) and B(3) for step 1, more later)
+          constexpr int VM_MID = NS == 4 ? APT + NB : NB;
           __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(0x0F70 | (NB & 15) | ((NB >> 4) << 14));
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_MID & 15) | ((VM_MID >> 4) << 14));
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
@@ -737,13 +754,13 @@ void mfma_gemm_kernel(MfmaArgs a) {
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[mt], Bq[j & 1][t], acc[mt][t]);
-          // R(step + 3) and A(step + 2) go out in sub-steps 2 and 3, the pieces spread over
-          // both; every piece precedes B(step + 3), as the waits assume
+          // R(step + AHEAD + 1) and A(step + AHEAD) go out in sub-steps 2 and 3, the pieces
+          // spread over both; every piece precedes B(step + 3), as the waits assume
           if (mt == 0 && j >= 2) {
-            if (j == 2) issue_sz(step + 3, sSn);
+            if (j == 2) issue_sz(step + AHEAD + 1, sSn);
 #pragma unroll
             for (int i = 0; i < APT; ++i)
-              if ((i * 2) / APT == j - 2) issue_a_piece(step + 2, sAn, i);
+              if ((i * 2) / APT == j - 2) issue_a_piece(step + AHEAD, sAn, i);
           }
 #pragma unroll
           for (int q = 0; q < PPM; ++q) {
@@ -781,11 +798,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // loop early (early exits make the accumulators spill).  A padded step reads its
   // activations out of range, i.e. zeros, so its MFMAs add exact zeros whatever the
   // (finite) weights of that step dequantize to.
-  const int nsteps3 = (nsteps + 2) / 3 * 3;
-  for (int step = 0; step < nsteps3; step += 3) {
+  const int nstepsR = (nsteps + NS - 1) / NS * NS;
+  for (int step = 0; step < nstepsR; step += NS) {
     step_body(step, std::integral_constant<int, 0>{});
     step_body(step + 1, std::integral_constant<int, 1>{});
     step_body(step + 2, std::integral_constant<int, 2>{});
+    if constexpr (NS == 4) step_body(step + 3, std::integral_constant<int, 3>{});
   }
   // the two out-of-range A loads of the last steps are still writing (zeros) into LDS:
   // let them land before the workgroup can finish and its LDS be handed to another
