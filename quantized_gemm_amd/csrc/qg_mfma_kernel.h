@@ -22,8 +22,8 @@
 // [w 256/CW, (w+1) 256/CW), so that every weight is dequantized exactly once per tile.
 // 16-bit paths use 8 waves of 32 columns (two waves per SIMD: one wave's dequant VALU
 // work co-executes with the other's MFMAs; MoE blocks of 128 rows keep 4 waves of 64),
-// e4m3 uses 4 waves of 64.  Activations go HBM -> LDS directly through a ring of three
-// stages, one 128-byte row segment per K step with a 16-byte XOR swizzle by row bits
+// e4m3 uses 4 waves of 64.  Activations go HBM -> LDS directly through a ring of four
+// stages (16-bit) or three (byte operands), one 128-byte row segment per K step with a 16-byte XOR swizzle by row bits
 // 1..3 (conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
 // prefetched two or three K steps ahead; the scale and zero records of a step travel
 // with the activations into LDS (two loads per workgroup and step, not one per lane).
@@ -794,7 +794,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
       load_b(step + DIST, bw[SL]);
     }
   };
-  // The step count is padded to a multiple of three rather than leaving the unrolled
+  // The step count is padded to a multiple of NS rather than leaving the unrolled
   // loop early (early exits make the accumulators spill).  A padded step reads its
   // activations out of range, i.e. zeros, so its MFMAs add exact zeros whatever the
   // (finite) weights of that step dequantize to.
