@@ -1,7 +1,7 @@
 """Reference token-to-expert sort and padding for the indexed MoE path.  TEST INFRASTRUCTURE ONLY.
 
-"Humming" (wiki article), "Device and workload selection": the indexed path gathers
-input rows through routing indices.  The pages give no more than that, so every rule
+"Humming" (wiki article), "Device and workload selection": in the index-routed MoE
+form each activation row is fetched by way of the routing table.  The page says no more, so every rule
 below is a reading (each is listed in the design notes).  Stability makes the
 result unique, so the GPU output must equal it byte for byte.
 

@@ -20,9 +20,9 @@
 //
 // Tile: BM x 256 per workgroup, CW waves, wave w owning all BM rows of the columns
 // [w 256/CW, (w+1) 256/CW), so that every weight is dequantized exactly once per tile.
-// 16-bit paths use 8 waves of 32 columns (two waves per SIMD: one wave's dequant VALU
-// work co-executes with the other's MFMAs; MoE blocks of 128 rows keep 4 waves of 64),
-// e4m3 uses 4 waves of 64.  Activations go HBM -> LDS directly through a ring of four
+// Tiles use 8 waves of 32 columns (two waves per SIMD: one wave's dequant VALU work
+// co-executes with the other's MFMAs); only MoE blocks of 128 rows with 16-bit
+// activations or with e2m1 weights under e4m3 activations keep 4 waves of 64.  Activations go HBM -> LDS directly through a ring of four
 // stages (16-bit) or three (byte operands), one 128-byte row segment per K step with a 16-byte XOR swizzle by row bits
 // 1..3 (conflict-free 16-byte fragment reads); weights go straight from HBM into VGPRs,
 // prefetched two or three K steps ahead; the scale and zero records of a step travel
