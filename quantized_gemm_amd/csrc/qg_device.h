@@ -135,22 +135,24 @@ __device__ __forceinline__ u32x4 fp4_to_16(uint32_t w, float scale) {
 }
 
 // int4 (two's complement, QUAD order) -> 8 e4m3 bytes in k order (2 dwords).
-// Table lookup with v_perm_b32: low 3 bits index one of two 8-entry tables
-// (q = 0..7 and q = -8..-1); bit 3 chooses between them through a byte mask built by
-// v_perm's constant selectors (12 -> 0x00, 13 -> 0xFF).  Every int4 value is an exact
+// Table lookup with v_perm_b32: the low 3 bits of a code index two 8-entry tables
+// (q = 0..7 and q = -8..-1) held in register pairs, and a third v_perm picks, byte by
+// byte, the entry of the table that the code's bit 3 names (selector byte i + 4 * bit 3).
+// The nibbles are taken in place: bit 3 of byte i's low (high) nibble moved to bit 2 by a
+// shift of 1 (5).  Six or seven operations per 4 weights.  Every int4 value is an exact
 // e4m3 value, so the conversion is lossless.
-__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t x /* 4 nibbles, one per byte */) {
-  const uint32_t idx = x & 0x07070707u;
+template <int SH>   // 0: the low nibble of each byte, 4: the high nibble
+__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t w) {
+  const uint32_t idx = (w >> SH) & 0x07070707u;
   const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, idx);
   const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, idx);
-  const uint32_t sel = ((x >> 3) & 0x01010101u) | 0x0C0C0C0Cu;
-  const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, sel);
-  return (neg & mask) | (pos & ~mask);
+  const uint32_t sel = ((w >> (SH + 1)) & 0x04040404u) | 0x03020100u;
+  return __builtin_amdgcn_perm(neg, pos, sel);
 }
 __device__ __forceinline__ u32x2 int4q_to_e4m3(uint32_t w) {
   u32x2 r;
-  r[0] = int4x4_to_e4m3(w & 0x0F0F0F0Fu);          // positions 0,2,4,6 = elements 0..3
-  r[1] = int4x4_to_e4m3((w >> 4) & 0x0F0F0F0Fu);   // positions 1,3,5,7 = elements 4..7
+  r[0] = int4x4_to_e4m3<0>(w);   // positions 0,2,4,6 = elements 0..3
+  r[1] = int4x4_to_e4m3<4>(w);   // positions 1,3,5,7 = elements 4..7
   return r;
 }
 
