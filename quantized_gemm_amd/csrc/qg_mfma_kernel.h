@@ -372,9 +372,9 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // s+1.  e4m3 weights go to the MFMA as they are: DIST = 2, so that one slot is always
   // idle and its registers free for other values.  Vector-memory issue order, kept by
   // sched_barrier: [B(0)] R(1) A(0) B(DIST-2) R(2) A(1) B(DIST-1), then per step s R(s+3)
-  // and A(s+2) (16-bit: in sub-steps 2 and 3, after the mid-step barrier; byte operands:
-  // spread over the step's MFMAs, or at the top) and B(s+DIST) at the bottom (DIST = 3),
-  // spread after A(s+2) (DIST = 2; int4 -> e4m3: before it), or right after it.
+  // and A(s+AHEAD) (16-bit: in sub-steps 2 and 3, after the mid-step barrier; byte operands:
+  // spread over the step's MFMAs, or at the top) and B(s+DIST) spread after them (int4 ->
+  // e4m3: before them), or right after them at the top.
   // R(t) are the scale / zero records of step t (16-bit paths; one load on waves 0 and 1
   // only), issued with A(t-1) into that stage's region, so they land when A(t-1) does and
   // are read at the top of step t-1.  Where a stage is published (the top of its step for
@@ -784,13 +784,19 @@ void mfma_gemm_kernel(MfmaArgs a) {
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[mt][t] = mfma32x32x16<AF>(Af[mt], Bq[j & 1][t], acc[mt][t]);
-          // R(step + AHEAD + 1) and A(step + AHEAD) go out in sub-steps 2 and 3, the pieces
-          // spread over both; every piece precedes B(step + 3), as the waits assume
-          if (mt == 0 && j >= 2) {
-            if (j == 2) issue_sz(step + AHEAD + 1, sSn);
+          // R(step + AHEAD + 1), A(step + AHEAD) and B(step + 3) go out in sub-steps 2 and 3,
+          // records first, then one piece or weight unit every 2 MT / (APT + NB) row tiles
+          // (all weights after every piece, as the waits assume)
+          if (j >= 2) {
+            if (j == 2 && mt == 0) issue_sz(step + AHEAD + 1, sSn);
+            const int slot = (j - 2) * MT + mt;
+            constexpr int NL16 = APT + NB;
 #pragma unroll
-            for (int i = 0; i < APT; ++i)
-              if ((i * 2) / APT == j - 2) issue_a_piece(step + AHEAD, sAn, i);
+            for (int k = 0; k < NL16; ++k) {
+              if (k * 2 * MT / NL16 != slot) continue;
+              if (k < APT) issue_a_piece(step + AHEAD, sAn, k);
+              else load_b_unit(step + DIST, bw[SL], (k - APT) / BU, (k - APT) % BU);
+            }
           }
 #pragma unroll
           for (int q = 0; q < PPM; ++q) {
@@ -817,11 +823,6 @@ void mfma_gemm_kernel(MfmaArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
-    // DIST = 3: weights and scales of step + 3 into this step's slot, now free
-    if constexpr (DIST == 3) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(step + DIST, bw[SL]);
     }
   };
   // The step count is padded to a multiple of NS rather than leaving the unrolled
