@@ -207,8 +207,6 @@ StreamTile stream_tile(int64_t rows, int64_t n, int w_type) {
 constexpr int kCUs = 256;
 constexpr int64_t kStreamMaxRows = 64;
 
-// The block-scaled e4m3 kernel uses 128-row tiles only.
-bool mfma_rows256(const PathInfo& pi) { return pi.wp_mfma != WP_FP8_BLOCK; }
 
 // Split K over workgroups when 128-row tiles would fill at most half of the CUs (above
 // that, writing and re-reading the fp32 partials costs more than the idle CUs):
@@ -230,10 +228,10 @@ int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
 MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo& pi) {
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
-  t.bm = (mfma_rows256(pi) && ((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
+  t.bm = (((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
   // experiment-only override of the row tile (QG_MFMA_BM=128|256)
   static const char* ov = getenv("QG_MFMA_BM");
-  if (ov && mfma_rows256(pi) && (atoi(ov) == 128 || atoi(ov) == 256)) t.bm = atoi(ov);
+  if (ov && (atoi(ov) == 128 || atoi(ov) == 256)) t.bm = atoi(ov);
   const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ntiles;
   t.grid_x = (unsigned)tiles;
   t.grid_y = 1;
@@ -276,22 +274,10 @@ int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
 }
 
 // Block-scaled e4m3 above the streaming sizes (and at every size under the batch-invariant
-// flag): 128 x 256 tiles with a promotion per 128-wide step; dense grids with at most half a
-// workgroup per CU split K over up to 8 workgroups (whole steps, at least two per slice).
+// flag): the MFMA kernel's tiles and K split (its promotion per 128-wide step leaves the split-K
+// partials scaled, so their reduction only adds them).
 bool is_block(const PathInfo& pi) { return pi.wp_small == WP_FP8_BLOCK; }
-MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) {
-  MfmaTile t{};
-  t.bm = 128;
-  const int64_t tiles = ((rows + 127) / 128) * ((n + 255) / 256);
-  t.grid_x = (unsigned)tiles;
-  t.grid_y = 1;
-  t.ksplit = 1;
-  const int64_t steps = k / 128;
-  if (!pi.binv)
-    while (t.ksplit < 8 && tiles * t.ksplit * 2 <= kCUs && steps % (t.ksplit * 2) == 0 && steps / (t.ksplit * 2) >= 2)
-      t.ksplit *= 2;
-  return t;
-}
+MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) { return mfma_tile(rows, n, k, 128, pi); }
 
 // Workspace of a dense call: the split-K partial sums.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
@@ -520,14 +506,14 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
     const double busy = mean + 3.0 * sqrt(mean);
     return busy <= 16 ? 16 : busy <= 32 ? 32 : busy <= 64 ? 64 : 128;
   }
-  if (pi.binv) return (mean < 512 || !mfma_rows256(pi)) ? 128 : 256;   // MFMA blocks at every size
+  if (pi.binv) return mean < 512 ? 128 : 256;   // MFMA blocks at every size
   if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
   if (mean + 3.0 * sqrt(mean) <= 64) {
     if (mean <= 16) return 16;
     if (mean <= 32) return 32;
     return 64;
   }
-  if (mean < 512 || !mfma_rows256(pi)) return 128;
+  if (mean < 512) return 128;
   return 256;
 }
 
@@ -596,7 +582,6 @@ qg_status qg_moe_gemm(const qg_prepared* p, const void* x, const void* x_scale, 
   if (block_m != 4 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256)
     return QG_ERR_UNSUPPORTED;
   if (pi.af == A_FP4 && (block_m == 4 || block_m == 256)) return QG_ERR_UNSUPPORTED;
-  if (block_m == 256 && !mfma_rows256(pi)) return QG_ERR_UNSUPPORTED;
   if (pi.binv && block_m <= kStreamMaxRows) return QG_ERR_UNSUPPORTED;   // one MMA type for every size
   if (tokens * topk > (int64_t)1 << 30 || !fits_rsrc(p, tokens)) return QG_ERR_UNSUPPORTED;
   s = check_arch();

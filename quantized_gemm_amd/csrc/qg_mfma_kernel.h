@@ -12,6 +12,10 @@
 //   * e2m1: hardware e2m1 -> bf16/f16 conversion with the UE8M0 scale folded in;
 //   * e4m3 x e4m3: fp8 MFMA (32x32x64) with the per-token / per-channel scales applied
 //     in the epilogue;
+//   * e4m3 x e4m3 with 128 x 128 weight-block and per-(row, 128-K) activation scales: each
+//     128-wide step's product from zero, promoted by (row scale x block scale); the weights
+//     are the MFMAs' first operand, so a lane's products share one activation row and one
+//     row scale;
 //   * e4m3 x e2m1 (W4A8 MXFP4): no dequantization at all, the e2m1 codes and their UE8M0
 //     block scales are operands of the scaled fp8/fp4 MFMA; per-token scale in the epilogue;
 //   * e2m1 x e2m1 (W4A4 MXFP4): both operands and both UE8M0 exponents go to the scaled
@@ -43,6 +47,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool F8 = (AF == A_FP8) || F4A;          // byte operands to scaled / fp8 MFMAs as stored
   constexpr bool FP4B = (AF == A_FP8) && WP == WP_FP4;   // e4m3 activations with e2m1 weights
   constexpr bool I4F8 = (AF == A_FP8) && WP == WP_INT4Q_FP8;   // int4 weights converted to e4m3 here
+  constexpr bool BLK = (AF == A_FP8) && WP == WP_FP8_BLOCK;     // e4m3 x e4m3 with 128 x 128 block scales
   constexpr int AB = F8 ? 1 : 2;
   constexpr int BK = F4A ? 256 : F8 ? 128 : 64;   // K per step; one LDS row segment = 128 bytes
   constexpr int NTHR = 64 * CW;              // CW waves, each owning BN / CW columns and all BM rows
@@ -79,7 +84,8 @@ void mfma_gemm_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sS3[NS == 4 ? SREG : 16];
   // e2m1 activations: the step's UE8M0 exponents of each tile row (8 bytes: K groups
   // 8 step .. 8 step + 7), one region per activation stage, loaded with that stage
-  constexpr int XSB = F4A ? BM * 8 : 16;
+  // block scales: the step's float scale of each tile row
+  constexpr int XSB = F4A ? BM * 8 : BLK ? BM * 4 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t sX0[XSB];
   __shared__ __attribute__((aligned(16))) uint8_t sX1[XSB];
   __shared__ __attribute__((aligned(16))) uint8_t sX2[XSB];
@@ -111,7 +117,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
     const int mtiles = (int)((a.m + BM - 1) / BM);
     const int ntiles = (int)gridDim.x / mtiles;
     const int id = blockIdx.x;
-    const int64_t rowb = F4A ? a.k / 2 : (int64_t)a.k * AB, colb = WP == WP_FP8 ? a.k : a.k / 2;   // bytes per row / column
+    const int64_t rowb = F4A ? a.k / 2 : (int64_t)a.k * AB, colb = (WP == WP_FP8 || BLK) ? a.k : a.k / 2;   // bytes per row / column
     int xr = 0;
     int64_t best = 0;
     for (int cand = 1; cand <= 8; cand <<= 1) {
@@ -154,7 +160,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // sums (the host makes the slices whole scale groups); otherwise all of K.
   const int nsteps = SPLIT ? a.k / BK / a.ksplit : a.k / BK;
   const int kstep0 = SPLIT ? (int)blockIdx.z * nsteps : 0;
-  const int64_t kun = WP == WP_FP8 ? (a.k >> 4) : (a.k >> 5);   // 16-byte units along K per column
+  const int64_t kun = (WP == WP_FP8 || BLK) ? (a.k >> 4) : (a.k >> 5);   // 16-byte units along K per column
   const int ngroups = a.group == 0 ? 1 : a.k / a.group;
   const uint8_t* wbase = a.w + (int64_t)expert * a.w_expert_bytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)a.w_expert_bytes);
@@ -187,18 +193,28 @@ void mfma_gemm_kernel(MfmaArgs a) {
   // e2m1 activations: dword h of tile row r's step exponents comes from thread 2r + h (a
   // wave-uniform subset of the threads), into region + 4 tid; issued just before the same
   // step's activations, so the wait for those covers it too.
+  // Block scales: the float scale of tile row r for the step comes from thread r the same way.
   int xs_off = -1;
   if constexpr (F4A) {
     if (tid < 2 * BM) {
       const int tok = sRowTok[tid >> 1];
       xs_off = tok < 0 ? -1 : tok * (a.k >> 5) + 4 * (tid & 1);
     }
+  } else if constexpr (BLK) {
+    if (tid < BM) {
+      const int tok = sRowTok[tid];
+      xs_off = tok < 0 ? -1 : tok * (a.k >> 7) * 4;
+    }
   }
-  const __amdgpu_buffer_rsrc_t xsr = make_rsrc(a.x_scale, F4A ? (uint32_t)(a.x_rows * (a.k >> 5)) : 0u);
+  const __amdgpu_buffer_rsrc_t xsr =
+      make_rsrc(a.x_scale, F4A ? (uint32_t)(a.x_rows * (a.k >> 5)) : BLK ? (uint32_t)(a.x_rows * (a.k >> 7) * 4) : 0u);
   auto issue_xs = [&](int step, uint8_t* reg) {
     if constexpr (F4A) {
       if (tid < 2 * BM)
         bload4_lds(xsr, reg + (tid & ~63) * 4, xs_off < 0 || step >= nsteps ? kOOB : xs_off + 8 * (kstep0 + step));
+    } else if constexpr (BLK) {
+      if (tid < BM)
+        bload4_lds(xsr, reg + (tid & ~63) * 4, xs_off < 0 || step >= nsteps ? kOOB : xs_off + 4 * (kstep0 + step));
     }
   };
 
@@ -334,6 +350,13 @@ void mfma_gemm_kernel(MfmaArgs a) {
       } else if constexpr (WP == WP_FP4) {
         const int64_t gi = (int64_t)(kstep0 + step) * 2 + g;   // group 32 == unit
         s[t] = scale_to_f32<ST>(a.s, (((int64_t)expert * nb_count + nb) * ngroups + gi) * 16 + c);
+        zs[t] = 0.f;
+      } else if constexpr (BLK) {
+        // the weight block's scale: the wave's columns lie inside one 128-column block, so
+        // the value is uniform over the wave
+        const int64_t nblk = a.n >> 7;
+        const int64_t blk = min(nblk - 1, (col0 + 32 * t) >> 7);
+        s[t] = ((const float*)a.s)[((int64_t)expert * nblk + blk) * (a.k >> 7) + kstep0 + step];
         zs[t] = 0.f;
       } else if constexpr (I4F8) {
         // one step (128 K) lies inside one scale group: the step's products are promoted by it
@@ -628,6 +651,63 @@ void mfma_gemm_kernel(MfmaArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else if constexpr (BLK) {
+      // Block scales: the step is one 128-wide block of K.  The weights are the MFMAs' first
+      // operand, so lane (r, g) of a product holds one activation row (32 mt + r) and 16 of the
+      // tile's columns (8(i/4) + 4g + i%4), and the promotion acc += (sa[row] * sw) * P needs
+      // one row scale per lane and row tile (sw is uniform over the wave: its 32 columns lie
+      // inside one 128-column block).  Both operands give the lane the same 32 K (chunks
+      // 4g + 2j and 4g + 2j + 1 of the row segment for MFMA j).  Per row tile two MFMAs from
+      // zero give P, promoted LAG row tiles later; fragments are read one MFMA ahead.
+      auto read_a8b = [&](int mt, int j) -> i32x8 {
+        const int row = 32 * mt + r;
+        const int lc0 = 4 * g + 2 * j;
+        const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * (lc0 ^ ((row >> 1) & 7)));
+        const u32x4 a1 = *(const u32x4*)(sAb + row * ROWB + 16 * ((lc0 + 1) ^ ((row >> 1) & 7)));
+        i32x8 A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = (int)a1[i]; }
+        return A;
+      };
+      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // (256-row tiles have no registers for a second product buffer: 64 bytes per lane spill)
+      constexpr int LAG = BM == 256 ? 0 : 1;
+      i32x8 Bw[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { Bw[t][j][i] = (int)b0[t][2 * j][i]; Bw[t][j][4 + i] = (int)b0[t][2 * j + 1][i]; }
+      i32x8 Ai[2];
+      f32x16 P[LAG + 1][NT];
+      Ai[0] = read_a8b(0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT + LAG; ++mt) {
+        if (mt < MT) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int q = 2 * mt + j;
+            if (q + 1 < 2 * MT) Ai[(q + 1) & 1] = read_a8b((q + 1) >> 1, (q + 1) & 1);
+            if constexpr (SPREAD) spread_loads(step, q, 2 * MT, sAn, bw[SL]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              P[mt % (LAG + 1)][t] = mfma32x32x64_fp8(Bw[t][j], Ai[q & 1], j == 0 ? zero16 : P[mt % (LAG + 1)][t]);
+          }
+        }
+        const int pm = mt - LAG;                       // row tile promoted now
+        if (pm >= 0) {
+          const float sa = *(const float*)(sXb + 4 * (32 * pm + r));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const float c = sa * scl[S][t];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[pm][t][i] = __builtin_fmaf(c, P[pm % (LAG + 1)][t][i], acc[pm][t][i]);
+            keep_in_vgprs(acc[pm][t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else if constexpr (I4F8) {
       // The lane's two units of this step were converted during the previous step (Bc): each
       // is the 32-byte e4m3 B operand of one 32x32x64 MFMA (k = 64u + 32g .. of the step, in k
@@ -868,6 +948,15 @@ void mfma_gemm_kernel(MfmaArgs a) {
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+          if constexpr (BLK) {
+            // transposed products (scales applied): lane (r, g) holds tile row r, columns
+            // 8(i/4) + 4g + i%4 of tile t
+            if (r / CR != h) continue;
+            const int rl = r - CR * h, cl = 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
+            if constexpr (SPLIT) *(float*)(ep + rl * PITCH + cl * 4) = acc[mt][t][i];
+            else *(uint16_t*)(ep + rl * PITCH + cl * 2) = f32_to_out<OF>(acc[mt][t][i]);
+            continue;
+          }
           if ((8 * (i >> 2)) / CR != h) continue;              // rows of element i: 8(i/4) + 0..7
           const int rl = 8 * (i >> 2) + 4 * g + (i & 3) - CR * h;
           float v = acc[mt][t][i];
@@ -911,7 +1000,7 @@ static void launch_mfma_one(const MfmaArgs& a, dim3 grid, hipStream_t st) {
   // (their blocks are many and short, and independent workgroups hide each other's barriers
   // better: measured 15% faster for 16-bit, 13-21% for e2m1 x e4m3, while dense 128-row
   // tiles gain ~10% from 8 waves and 4-wave e4m3-weight tiles spill).
-  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8 || WP == WP_INT4Q_FP8 || AF == A_FP4) ? 8 : 4;
+  constexpr int CW = (BM == 256 || !MOE || WP == WP_FP8 || WP == WP_FP8_BLOCK || WP == WP_INT4Q_FP8 || AF == A_FP4) ? 8 : 4;
   hipLaunchKernelGGL((mfma_gemm_kernel<WP, AF, OF, ST, ZERO, BM, MOE, SPLIT, CW>), grid, dim3(64 * CW), 0, st, a);
 }
 

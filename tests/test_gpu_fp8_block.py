@@ -68,12 +68,15 @@ def test_batch_invariant_rows():
         assert np.array_equal(got, ref[:m]), f"M={m}"
 
 
-@pytest.mark.parametrize("t", [1, 30, 60, 300])
+@pytest.mark.parametrize("t", [1, 30, 60, 300, 1100])
 def test_moe(t):
     layer, acts = synth.moe_w8a8_fp8_block(t=t, experts=4, topk=2, n=256, k=512, seed=t)
     p, buf = layers.prepare_layer(layer)
     bm = qg.moe_block_m(p, t, 2)
-    assert bm in (4, 16, 32, 64, 128)          # streaming blocks for few rows per expert, else 128
+    # streaming blocks for few rows per expert, else 128-row MFMA blocks; 256 from a mean of
+    # 512 rows per expert
+    assert bm in (4, 16, 32, 64, 128, 256)
+    assert (bm == 256) == (t == 1100)
     cs, cb = qg.moe_capacity(t, 2, 4, bm)
     s = torch.empty(cs, dtype=torch.int32, device="cuda")
     e = torch.empty(cb, dtype=torch.int32, device="cuda")

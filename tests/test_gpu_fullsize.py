@@ -92,6 +92,20 @@ def test_dense_w8a8_fp8_7168(c3, m):
     c3.check(m)
 
 
+@pytest.fixture(scope="module")
+def c3_block():
+    d = _Dense(*synth.dense_w8a8_fp8_block(m=4096, n=7168, k=7168, seed=0))
+    yield d
+    del d
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("m", [1, 64, 512, 4096])
+def test_dense_w8a8_fp8_block_7168(c3_block, m):
+    # 1 / 64 rows: streaming kernel; 512: 128-row tiles with K split; 4096: 256-row tiles
+    c3_block.check(m)
+
+
 def test_dense_w4a16_sym_f16_512x1024():
     d = _Dense(*synth.dense_w4a16_sym_f16(m=16, n=512, k=1024, seed=0))
     d.check(16)
