@@ -235,6 +235,20 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp4_fp4(i32x8 a, i32x8 b, int sa,
 __device__ __forceinline__ f32x16 mfma32x32x64_fp4_fp4(i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
+// The same with the scale bytes taken from byte J of each scale word (the instruction's
+// byte select: four steps' or quarters' exponents share one register)
+template <int J>
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4_fp4_b(i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, J, sa, J, sb);
+}
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4_fp4_byte(int j, i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
+  switch (j) {
+    case 0: return mfma32x32x64_fp4_fp4_b<0>(a, b, sa, sb, c);
+    case 1: return mfma32x32x64_fp4_fp4_b<1>(a, b, sa, sb, c);
+    case 2: return mfma32x32x64_fp4_fp4_b<2>(a, b, sa, sb, c);
+    default: return mfma32x32x64_fp4_fp4_b<3>(a, b, sa, sb, c);
+  }
+}
 
 template <int AF>
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
@@ -248,6 +262,18 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8_fp4(i32x8 a, i32x8 b, int sb, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, 127, 0, sb);
+}
+template <int J>
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8_fp4_b(i32x8 a, i32x8 b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, 127, J, sb);
+}
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8_fp4_byte(int j, i32x8 a, i32x8 b, int sb, f32x16 c) {
+  switch (j) {
+    case 0: return mfma32x32x64_fp8_fp4_b<0>(a, b, sb, c);
+    case 1: return mfma32x32x64_fp8_fp4_b<1>(a, b, sb, c);
+    case 2: return mfma32x32x64_fp8_fp4_b<2>(a, b, sb, c);
+    default: return mfma32x32x64_fp8_fp4_b<3>(a, b, sb, c);
+  }
 }
 
 // ---- loads -------------------------------------------------------------------------

@@ -618,35 +618,43 @@ void mfma_gemm_kernel(MfmaArgs a) {
       // 4 x MT MFMAs per step (K quarters j, row tiles mt), 32x32x64 with both operands e2m1:
       // lane (r, g) gives row r's K 64j + 32g .. + 31 (16 bytes, chunk 2j + g of the row
       // segment) and its exponent; fragments are read two MFMAs ahead as in the e4m3 loop
-      auto read_a4 = [&](int q, int& sa) -> i32x8 {
+      auto read_a4 = [&](int q) -> i32x8 {
         const int j = q / MT, mt = q % MT;
         const int row = 32 * mt + r;
         const u32x4 a0 = *(const u32x4*)(sAb + row * ROWB + 16 * ((2 * j + g) ^ ((row >> 1) & 7)));
-        sa = sXb[row * 8 + 2 * j + g];
         i32x8 A;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { A[i] = (int)a0[i]; A[4 + i] = 0; }
         return A;
       };
+      // The lane's four exponents of row 32 mt + r (groups 2j + g of the step, j = 0..3) as
+      // bytes 0..3 of one word: one 8-byte read per row tile and a byte permute; each MFMA
+      // picks its byte (and the weight word's byte j) with the instruction's byte select.
+      uint32_t ea[MT];
+      const uint32_t esel = g ? 0x07050301u : 0x06040200u;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x2 e = *(const u32x2*)(sXb + (32 * mt + r) * 8);
+        ea[mt] = __builtin_amdgcn_perm(e[1], e[0], esel);
+      }
       // (256-row tiles read one MFMA ahead: their accumulators leave no room for a third set)
       constexpr int NQ = 4 * MT;
       constexpr int AH = BM == 256 ? 1 : 2;      // fragments read ahead
       i32x8 Af4[AH + 1];
-      int sa4[AH + 1];
 #pragma unroll
-      for (int q = 0; q < AH; ++q) Af4[q] = read_a4(q, sa4[q]);
+      for (int q = 0; q < AH; ++q) Af4[q] = read_a4(q);
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int j = q / MT, mt = q % MT;
-        if (q + AH < NQ) Af4[(q + AH) % (AH + 1)] = read_a4(q + AH, sa4[(q + AH) % (AH + 1)]);
+        if (q + AH < NQ) Af4[(q + AH) % (AH + 1)] = read_a4(q + AH);
         if constexpr (SPREAD) spread_loads(step, q, NQ, sAn, bw[SL]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           i32x8 B;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { B[i] = (int)b0[t][j][i]; B[4 + i] = 0; }
-          acc[mt][t] = mfma32x32x64_fp4_fp4(Af4[q % (AH + 1)], B, sa4[q % (AH + 1)],
-                                            (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu), acc[mt][t]);
+          acc[mt][t] = mfma32x32x64_fp4_fp4_byte(j, Af4[q % (AH + 1)], B, (int)ea[mt], (int)__float_as_uint(scl[S][t]),
+                                                 acc[mt][t]);
           keep_in_vgprs(acc[mt][t]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -815,8 +823,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if constexpr (FP4B)
-            acc[mt][t] = mfma32x32x64_fp8_fp4(Af8[q % 3], B[t], (int)((__float_as_uint(scl[S][t]) >> (8 * j)) & 0xFFu),
-                                              acc[mt][t]);
+            acc[mt][t] = mfma32x32x64_fp8_fp4_byte(j, Af8[q % 3], B[t], (int)__float_as_uint(scl[S][t]), acc[mt][t]);
           else
             acc[mt][t] = mfma32x32x64_fp8(Af8[q % 3], B[t], acc[mt][t]);
           // Nothing else depends on an MFMA result, and the code generator otherwise sinks
