@@ -229,21 +229,10 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
   t.bm = (((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
-  // experiment-only override of the row tile (QG_MFMA_BM=128|256)
-  static const char* ov = getenv("QG_MFMA_BM");
-  if (ov && (atoi(ov) == 128 || atoi(ov) == 256)) t.bm = atoi(ov);
   const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ntiles;
   t.grid_x = (unsigned)tiles;
   t.grid_y = 1;
   t.ksplit = t.bm == 128 ? split_for(tiles, k, group, pi) : 1;
-  // experiment-only override of the split (QG_KSPLIT=1|2|4|8; slices must stay whole groups)
-  static const char* ks = getenv("QG_KSPLIT");
-  if (ks && t.bm == 128 && !pi.binv) {
-    const int v = atoi(ks);
-    const int64_t bk = pi.af == A_FP8 ? 128 : 64;
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / bk) % v == 0 && (group <= 0 || (k / v) % group == 0))
-      t.ksplit = v;
-  }
   return t;
 }
 
@@ -258,12 +247,6 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
 constexpr int64_t kTinyWeights = (int64_t)1 << 22;
 int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
   if (rows <= 4 || n * k <= kTinyWeights) return 1;
-  // experiment-only override (QG_STREAM_SPLIT=1|2|4|8; slices must stay whole groups)
-  static const char* ov = getenv("QG_STREAM_SPLIT");
-  if (ov) {
-    const int v = atoi(ov);
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && (k / 128) % v == 0 && (group <= 0 || (k / v) % group == 0)) return v;
-  }
   const int64_t groups = (n / 16 + 7) / 8;
   const int64_t chunks = k / 128;
   int sp = 1;
