@@ -236,7 +236,7 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   return t;
 }
 
-// Dense weight streaming for 5..64 rows: workgroups of 8 column blocks (128 columns) x 1 K
+// Dense weight streaming for 5..32 rows (block-scaled: 64): workgroups of 8 column blocks (128 columns) x 1 K
 // part, with K split over up to 8 workgroups so that about one workgroup per CU remains.
 // Each workgroup then stages only its slice of K for its rows (one LDS round at 16 rows)
 // instead of all of K; the fp32 partials are summed by the split-K reduction.  1..4 rows
@@ -260,16 +260,23 @@ int stream_split(int64_t rows, int64_t n, int64_t k, int group) {
 // flag): the MFMA kernel's tiles and K split (its promotion per 128-wide step leaves the split-K
 // partials scaled, so their reduction only adds them).
 bool is_block(const PathInfo& pi) { return pi.wp_small == WP_FP8_BLOCK; }
+
+// Dense rows up to which the streaming kernel runs: 32, where its 64-row tiles lose to the
+// MFMA kernel's 128-row tiles with K split (dense W4A16 N = K = 8192: 40..64 rows 30.6-31.7 us
+// streamed, 23.6-25.4 us on the MFMA kernel; e4m3 and e2m1 x e4m3 weights alike, at 32 rows
+// and below the streaming kernel is faster), 64 for block-scaled e4m3 (streamed 15-22 us
+// against 21-24 us at 17..64 rows).
+int64_t dense_stream_max(const PathInfo& pi) { return is_block(pi) ? 64 : 32; }
 MfmaTile block_tile(int64_t rows, int64_t n, int64_t k, const PathInfo& pi) { return mfma_tile(rows, n, k, 128, pi); }
 
 // Workspace of a dense call: the split-K partial sums.
 size_t dense_workspace(const qg_prepared* p, const PathInfo& pi, int64_t m) {
   if (pi.af == A_FP4) return 0;   // W4A4 splits K only inside a workgroup
-  if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
+  if (is_block(pi) && (m > dense_stream_max(pi) || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     return t.ksplit > 1 ? (size_t)t.ksplit * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
   }
-  if (m <= kStreamMaxRows && !pi.binv) {
+  if (m <= dense_stream_max(pi) && !pi.binv) {
     const int sp = stream_split(m, p->desc.n, p->desc.k, p->desc.group_k);
     return sp > 1 ? (size_t)sp * (size_t)m * (size_t)p->desc.n * sizeof(float) : 0;
   }
@@ -418,7 +425,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
     if (!launch_w4a4(a, bm, false, pi.of, 1, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
     return launched();
   }
-  if (is_block(pi) && (m > kStreamMaxRows || pi.binv)) {
+  if (is_block(pi) && (m > dense_stream_max(pi) || pi.binv)) {
     const MfmaTile t = block_tile(m, p->desc.n, p->desc.k, pi);
     if (t.ksplit > 1) {
       const size_t need = dense_workspace(p, pi, m);
@@ -433,7 +440,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
     if (t.ksplit > 1 && !launch_split_reduce(a, false, false, pi.of, (hipStream_t)stream)) return QG_ERR_UNSUPPORTED;
     return launched();
   }
-  const bool mfma = m > kStreamMaxRows || pi.binv;   // batch-invariant: one MMA type for every M
+  const bool mfma = m > dense_stream_max(pi) || pi.binv;   // batch-invariant: one MMA type for every M
   if (mfma) {
     const MfmaTile t = mfma_tile(m, p->desc.n, p->desc.k, p->desc.group_k, pi);
     if (t.ksplit > 1) {

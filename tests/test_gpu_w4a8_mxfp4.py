@@ -2,7 +2,7 @@
 activations), through the C ABI.
 
 The product runs on the scaled fp8 x fp4 MFMAs of gfx950 with the weights as stored: the
-streaming kernel (16x16x128) for up to 64 rows and MoE blocks up to 64, the MFMA kernel
+streaming kernel (16x16x128) for up to 32 rows and MoE blocks up to 64, the MFMA kernel
 (32x32x64) above, in 128- and 256-row tiles and split over K.  Bars: prepared bytes and
 read-back bit-exact; products max|Y - Y_ref| / max|Y_ref| <= 2e-2 (e4m3 activations), and
 much tighter in practice since the only rounding is the float32 accumulation and the
