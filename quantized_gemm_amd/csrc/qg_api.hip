@@ -484,25 +484,32 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   PathInfo pi;
   if (check_prepared(p, &pi) != QG_OK || tokens < 0 || topk <= 0) return 0;
   // With a mean of m rows per expert, counts spread about sqrt(m) (multinomial routing).
-  // The streaming family is kept while the busier experts, mean + 3 sqrt(mean) rows, fit
-  // in its largest block (64 rows): beyond that most experts would stream their weights
-  // two or more times, and 128-row MFMA blocks win.  Within the streaming family the
-  // block follows the mean (a bigger block re-stages more activation rows per round,
-  // which costs more than the occasional second pass over an expert's weights).
+  // About one routed row per expert (busy = mean + 3 sqrt(mean) <= 4) streams 4-row blocks; up to a
+  // mean of 16 rows, 16-row streaming blocks; above, 128-row MFMA blocks (256 from 512 rows
+  // per expert).  Measured against the alternatives at E = 128 top-8 (N = 4096, K = 7168) and
+  // E = 64 top-6 (N = 2816, K = 4096): 16-row blocks win up to a mean of 12-16 rows; 32- and
+  // 64-row streaming blocks lose to 128-row MFMA blocks (a mean of 36: MXFP4 900 -> 606 us,
+  // W4A8 int4 266 -> 135 us, W4A8 MXFP4 562 -> 398 us), except 32-row blocks with 16-bit
+  // activations up to a mean of 24 (a mean of 20: 561 against 591 us).  Block-scaled W8A8
+  // keeps its streaming blocks up to 64 rows (its streaming kernel wins there, dense too).
   const double rows = (double)tokens * topk;
   const double mean = rows / p->desc.num_experts;
-  if (pi.af == A_FP4) {   // W4A4 blocks: 16, 32, 64 or 128 rows, the busier experts' counts fitting
+  const double busy = mean + 3.0 * sqrt(mean);
+  if (pi.af == A_FP4) {
+    // W4A4: 16-row W4A4-kernel blocks while the busier experts fit them, else 128-row blocks
+    // (32- and 64-row blocks lost to them: E = 128 top-8, a mean of 8 / 16 / 24 / 36 rows,
+    // 446 / 491 / 581 / 650 -> 360 / 366 / 371 / 374 us)
+#ifdef QG_W44R
+    return busy <= QG_W44R ? 16 : 128;
+#endif
     if (pi.binv) return 128;
-    const double busy = mean + 3.0 * sqrt(mean);
-    return busy <= 16 ? 16 : busy <= 32 ? 32 : busy <= 64 ? 64 : 128;
+    return busy <= 16 ? 16 : 128;
   }
   if (pi.binv) return mean < 512 ? 128 : 256;   // MFMA blocks at every size
-  if (mean + 3.0 * sqrt(mean) <= 4) return 4;      // about one routed row per expert
-  if (mean + 3.0 * sqrt(mean) <= 64) {
-    if (mean <= 16) return 16;
-    if (mean <= 32) return 32;
-    return 64;
-  }
+  if (busy <= 4) return 4;
+  if (is_block(pi) && busy <= 64) return mean <= 16 ? 16 : mean <= 32 ? 32 : 64;
+  if (mean <= 16) return 16;
+  if (mean <= 24 && pi.af != A_FP8) return 32;
   if (mean < 512) return 128;
   return 256;
 }
