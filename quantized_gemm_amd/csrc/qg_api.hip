@@ -499,9 +499,6 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
     // W4A4: 16-row W4A4-kernel blocks while the busier experts fit them, else 128-row blocks
     // (32- and 64-row blocks lost to them: E = 128 top-8, a mean of 8 / 16 / 24 / 36 rows,
     // 446 / 491 / 581 / 650 -> 360 / 366 / 371 / 374 us)
-#ifdef QG_W44R
-    return busy <= QG_W44R ? 16 : 128;
-#endif
     if (pi.binv) return 128;
     return busy <= 16 ? 16 : 128;
   }
