@@ -403,8 +403,11 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
   a.x = x; a.x_scale = (const float*)x_scale; a.y = y; a.m = m; a.x_rows = m;
   a.ksplit = 1;
   if (pi.af == A_FP4) {
-    // enough 256-column tiles to fill the GPU and whole 256-wide K steps: the MFMA kernel
-    // (activations staged through LDS, 32x32x64 fp4 MFMAs), else the W4A4 kernel
+    // whole 256-wide K steps and either more than 128 rows or enough 256-column tiles to fill
+    // the GPU: the MFMA kernel (activations staged through LDS, 32x32x64 fp4 MFMAs), else the
+    // W4A4 kernel.  Above 128 rows the MFMA kernel wins even with fewer tiles than CUs
+    // (N = K = 8192, 192..768 rows: 35-40 us against 51-149 us); up to 128 rows the W4A4
+    // kernel does (27 against 35-40 us)
     if (!pi.binv && m > 64 && p->desc.k % 256 == 0) {
       MfmaTile t{};
       const int64_t ntiles = (p->desc.n + 255) / 256;
@@ -412,7 +415,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
       t.grid_x = (unsigned)(((m + t.bm - 1) / t.bm) * ntiles);
       t.grid_y = 1;
       t.ksplit = 1;
-      if (t.grid_x >= (unsigned)kCUs) {
+      if (t.grid_x >= (unsigned)kCUs || m > 128) {
         QG_LOG("gemm m=%lld n=%lld k=%lld -> fp4 mfma bm=%d grid=%u", (long long)m, (long long)p->desc.n,
                (long long)p->desc.k, t.bm, t.grid_x);
         if (!launch_mfma_gemm(a, t, WP_FP4, A_FP4, pi.of, S_UE8M0, false, false, (hipStream_t)stream))
