@@ -224,11 +224,23 @@ int split_for(int64_t tiles, int64_t k, int group, const PathInfo& pi) {
   return sp;
 }
 
+// 256-row tiles take about 7/8 of the time of two 128-row tiles (each weight is converted and
+// fed once per 256 rows instead of twice); with one workgroup per CU at a time a launch takes as
+// many tile times as it has rounds of workgroups, so 256 rows are taken when their rounds cost
+// less: dense W4A16 N = K = 8192 at M = 2048 (one round of 256-row tiles against two of 128)
+// 249 -> 220 us, W4A8 MXFP4 at M = 3072 (1.5 rounds of 256-row against 3 of 128) keeps 128
+// rows, 197 -> 178 us.
+bool rows256(int64_t rows, int64_t ntiles) {
+  const int64_t r256 = ((rows + 255) / 256 * ntiles + kCUs - 1) / kCUs;
+  const int64_t r128 = ((rows + 127) / 128 * ntiles + kCUs - 1) / kCUs;
+  return 2 * 7 * r256 < 8 * r128;
+}
+
 // Dense tiles (MoE tiles are built by qg_moe_gemm).
 MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo& pi) {
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
-  t.bm = (((rows + 255) / 256) * ntiles * 2 >= 3 * kCUs) ? 256 : 128;
+  t.bm = rows256(rows, ntiles) ? 256 : 128;
   const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ntiles;
   t.grid_x = (unsigned)tiles;
   t.grid_y = 1;
@@ -411,7 +423,7 @@ qg_status qg_gemm(const qg_prepared* p, const void* x, const void* x_scale, void
     if (!pi.binv && m > 64 && p->desc.k % 256 == 0) {
       MfmaTile t{};
       const int64_t ntiles = (p->desc.n + 255) / 256;
-      t.bm = ((m + 255) / 256) * ntiles * 2 >= 3 * kCUs ? 256 : 128;   // 256 rows: half the weight feed
+      t.bm = rows256(m, ntiles) ? 256 : 128;   // 256 rows: half the weight feed
       t.grid_x = (unsigned)(((m + t.bm - 1) / t.bm) * ntiles);
       t.grid_y = 1;
       t.ksplit = 1;
