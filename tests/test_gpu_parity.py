@@ -170,10 +170,10 @@ def test_moe_align_is_bit_exact(case):
     assert np.array_equal(e.cpu().numpy(), re_)
 
 
-def _run_moe(layer, acts, workspace=False):
+def _run_moe(layer, acts, workspace=False, bm=None):
     t, topk = acts.topk_ids.shape
     p, buf = layers.prepare_layer(layer)
-    bm = qg.moe_block_m(p, t, topk)
+    bm = bm or qg.moe_block_m(p, t, topk)
     s, e, n = _align_gpu(acts.topk_ids, layer.experts, bm)
     x, xs = layers.acts_to_dev(acts)
     y = torch.full((t * topk, layer.n), float("nan"), dtype=layers.out_dtype(layer), device="cuda")
@@ -262,11 +262,12 @@ def test_dense_w8a8_fp8_mfma_path(m):
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
 
 
-@pytest.mark.parametrize("t,experts", [(400, 4), (1100, 4)])
-def test_moe_w4a16_mxfp4_mfma_path(t, experts):
-    # 200 and 550 rows per expert: blocks of 128 and 256 rows
+@pytest.mark.parametrize("t,experts,bm", [(400, 4, None), (1100, 4, None), (1100, 4, 256)])
+def test_moe_w4a16_mxfp4_mfma_path(t, experts, bm):
+    # 200 and 550 rows per expert: 128-row blocks (e2m1 weights never take 256 by themselves),
+    # and 256-row blocks when the caller asks for them
     layer, acts = synth.moe_w4a16_mxfp4(t=t, experts=experts, topk=2, n=320, k=512, seed=11)
-    y = _run_moe(layer, acts)
+    y = _run_moe(layer, acts, bm=bm)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL16
 
 
@@ -290,7 +291,7 @@ def test_dense_w4a8_int4_to_fp8(m):
 
 @pytest.mark.parametrize("t", [400, 1000])
 def test_moe_w4a8_int4_mfma_path(t):
-    # 200 / 500 rows per expert (skewed router): blocks of 128 rows on the fp8 MFMA kernel
+    # 200 / 500 rows per expert (skewed router): blocks of 128 / 256 rows on the fp8 MFMA kernel
     layer, acts = synth.moe_w4a8_int4(t=t, experts=4, topk=2, n=256, k=512, seed=13)
     y = _run_moe(layer, acts)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8

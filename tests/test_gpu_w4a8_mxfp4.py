@@ -73,10 +73,10 @@ def test_dense_256_row_tiles_and_f16_output():
     assert R.relative_error(_dense(layer, acts, 70), R.dense_reference(layer, acts)) <= TOL8
 
 
-def _moe(layer, acts):
+def _moe(layer, acts, bm=None):
     t, topk = acts.topk_ids.shape
     p, buf = layers.prepare_layer(layer)
-    bm = qg.moe_block_m(p, t, topk)
+    bm = bm or qg.moe_block_m(p, t, topk)
     cs, cb = qg.moe_capacity(t, topk, layer.experts, bm)
     s = torch.empty(cs, dtype=torch.int32, device="cuda")
     e = torch.empty(cb, dtype=torch.int32, device="cuda")
@@ -91,11 +91,13 @@ def _moe(layer, acts):
     return bm, layers.out_bits_to_f64(y).reshape(t, topk, layer.n)
 
 
-@pytest.mark.parametrize("t", [1, 5, 40, 100, 300, 1100])
-def test_moe(t):
-    # block sizes 4 .. 64 (streaming), 128 and 256 (MFMA) as the routed rows per expert grow
+@pytest.mark.parametrize("t,bm", [(1, None), (5, None), (40, None), (100, None), (300, None), (1100, None),
+                                  (1100, 256)])
+def test_moe(t, bm):
+    # block sizes 4 and 16 (streaming), 128 (MFMA) as the routed rows per expert grow, and
+    # 256-row MFMA blocks when the caller asks for them
     layer, acts = synth.moe_w4a8_mxfp4(t=t, experts=8, topk=4, n=192, k=768, seed=t)
-    bm, y = _moe(layer, acts)
+    bm, y = _moe(layer, acts, bm)
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8, f"block {bm}"
 
 
