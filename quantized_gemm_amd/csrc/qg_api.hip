@@ -523,12 +523,13 @@ int32_t qg_moe_block_m(const qg_prepared* p, int64_t tokens, int32_t topk) {
   if (mean <= 16) return 16;
   if (mean <= 24 && pi.af != A_FP8) return 32;
   // 256-row blocks halve the weight conversion per FLOP and add padding rows: int4 weights
-  // converted to e4m3 take them from a mean of 256 rows (E = 64 top-6 skewed, K = 4096: a mean
-  // of 256 / 512 / 768 rows 386 / 663 / 943 -> 343 / 568 / 802 us), e2m1 weights never (E = 128
+  // converted to e4m3 take them from a mean of 128 rows (E = 64 top-6 skewed, K = 4096: a mean
+  // of 144 / 192 / 256 / 512 / 768 rows 240 / 319 / 386 / 663 / 943 -> 221 / 293 / 343 / 568 /
+  // 802 us; at 72 / 96 rows 128-row blocks win, 149 / 196 against 208 / 215 us), e2m1 weights never (E = 128
   // top-8: a mean of 512 / 768 / 1536 rows 3356 / 4742 / 9102 -> 3020 / 4419 / 8440 us with
   // 128-row blocks under 16-bit activations, 1929 / 2705 -> 1796 / 2534 us under e4m3), the
   // others from a mean of 512.
-  const double from256 = pi.wp_mfma == WP_INT4Q_FP8 ? 256 : pi.wp_mfma == WP_FP4 ? 1e300 : 512;
+  const double from256 = pi.wp_mfma == WP_INT4Q_FP8 ? 128 : pi.wp_mfma == WP_FP4 ? 1e300 : 512;
   return mean < from256 ? 128 : 256;
 }
 
