@@ -241,6 +241,24 @@ MfmaTile mfma_tile(int64_t rows, int64_t n, int64_t k, int group, const PathInfo
   MfmaTile t{};
   const int64_t ntiles = (n + 255) / 256;
   t.bm = rows256(rows, ntiles) ? 256 : 128;
+  // Few rows: 64-row tiles with K split when the split applies.  Half the rows per tile
+  // halve the partial sums written and read back; they double the weight conversion per FLOP,
+  // which the byte-operand paths barely have: 64-row tiles up to 64 rows (dense W4A16 8192^2
+  // at 33 / 64 rows 25.1 / 27.3 -> 20.1 / 23.7 us, slower at 96 / 128 rows), and up to 128
+  // rows for e4m3 and e2m1 x e4m3 weights (W4A8 MXFP4 at 96 / 128 rows 25.6 / 29.8 -> 19.8 /
+  // 21.2 us, block-scaled W8A8 27.8 / 29.3 -> 25.3 / 26.4 us).
+  const int64_t rows64 = pi.af == A_FP8 && pi.wp_mfma != WP_INT4Q_FP8 ? 128 : 64;
+  if (t.bm == 128 && rows <= rows64 && pi.af != A_FP4 && !pi.binv) {
+    const int64_t tiles64 = ((rows + 63) / 64) * ntiles;
+    const int sp64 = split_for(tiles64, k, group, pi);
+    if (sp64 > 1) {
+      t.bm = 64;
+      t.grid_x = (unsigned)tiles64;
+      t.grid_y = 1;
+      t.ksplit = sp64;
+      return t;
+    }
+  }
   const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ntiles;
   t.grid_x = (unsigned)tiles;
   t.grid_y = 1;

@@ -1030,6 +1030,10 @@ static bool launch_mfma_variant(const MfmaArgs& a, const MfmaTile& t, bool moe, 
       if (t.bm == 256) { launch_mfma_one<WP, AF, OF, ST, ZERO, 256, true>(a, grid, st); return true; }
     } else {
       if (t.ksplit > 1) {
+        if (t.bm == 64) {   // few rows: 64-row tiles, K split
+          launch_mfma_one<WP, AF, OF, ST, ZERO, 64, false, true>(a, dim3(t.grid_x, t.grid_y, t.ksplit), st);
+          return true;
+        }
         if (t.bm != 128) return false;
         launch_mfma_one<WP, AF, OF, ST, ZERO, 128, false, true>(a, dim3(t.grid_x, t.grid_y, t.ksplit), st);
         return true;
