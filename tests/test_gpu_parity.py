@@ -280,10 +280,10 @@ def test_moe_w8a8_fp8(t, experts):
     assert R.relative_error(y, R.moe_reference(layer, acts)) <= TOL8
 
 
-@pytest.mark.parametrize("m", [8, 100, 300])
+@pytest.mark.parametrize("m", [8, 48, 100, 300])
 def test_dense_w4a8_int4_to_fp8(m):
     # the W4A8 layer used densely (one expert): streaming path at 8 rows, fp8 MFMA with
-    # per-group promotion above 64 rows
+    # per-group promotion above 32 rows (48 rows: 64-row tiles with K split)
     layer, acts = synth.moe_w4a8_int4(t=m, experts=1, topk=1, n=320, k=1024, seed=12)
     y = _run_dense(layer, acts, m)
     assert R.relative_error(y, R.dense_reference(layer, acts)) <= TOL8
