@@ -415,6 +415,12 @@ void mfma_gemm_kernel(MfmaArgs a) {
   constexpr bool SPREAD = F8 && (!I4F8 || BM == 256);
   constexpr bool BFIRST = I4F8;
   constexpr int NL = APT + NT * BU;            // loads per thread and step
+  // Where a slot takes two loads (more loads than MFMAs: e4m3-weight 64-row tiles, 5 loads
+  // over 4), a scheduling barrier keeps them in this order: the wait counts (VM_A below)
+  // count the loads issued after a stage's last activation piece, and the scheduler may
+  // otherwise move that piece behind a weight load of the same slot (seen after an
+  // unrelated change: the stage was then read before it had landed).  Slots of one load are
+  // ordered by the barrier after each MFMA.
   auto spread_loads = [&](int step, int q, int nq, uint8_t* sAn, u32x4 (&bdst)[NT][BU]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
@@ -422,6 +428,7 @@ void mfma_gemm_kernel(MfmaArgs a) {
       const int kb = BFIRST ? k : k - APT;     // weight unit, if this load is one
       if (kb >= 0 && kb < NT * BU) load_b_unit(step + DIST, bdst, kb / BU, kb % BU);
       else issue_a_piece(step + AHEAD, sAn, BFIRST ? k - NT * BU : k);
+      if (NL > nq) __builtin_amdgcn_sched_barrier(0);
     }
   };
   u32x4 bw[NS][NT][BU];
